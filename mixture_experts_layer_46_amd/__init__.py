@@ -1,0 +1,157 @@
+"""MI355X-native token-choice Mixture-of-Experts layer forward.
+
+The layer runs in libmoe.so (hand-written HIP kernels for gfx950 behind a C ABI,
+include/moe.h).  This module only allocates torch device tensors for outputs and
+workspace and passes pointers and the current stream; it has no other compute path.
+
+    out = forward(x, w_gate, w_in, w_up, w_out, top_k, bias=None)
+
+x [T, H] (bf16 or fp32), w_gate [H, E] fp32, w_in / w_up [E, H, F], w_out [E, F, H]
+(w_up None for the two-layer SiLU FFN), bias [E] fp32 or None.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_F32, MOE_FFN_SILU2, MOE_FFN_SWIGLU, MOE_FLAG_BIAS_SELECT_ONLY,
+                   MOE_FLAG_NO_RENORM, MoeError, Shape, capacity_rows)
+
+__all__ = ["forward", "route", "route_from_logits", "permute", "grouped_ffn", "combine",
+           "router_stats", "make_shape", "Workspace", "Shape", "MoeError",
+           "MOE_FLAG_BIAS_SELECT_ONLY", "MOE_FLAG_NO_RENORM", "capacity_rows"]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU (the layer has no CPU path)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def make_shape(T, H, E, k, F, dtype=torch.bfloat16, swiglu=True, flags=0, capacity=0) -> Shape:
+    return Shape(T=T, H=H, E=E, k=k, F=F,
+                 dtype=MOE_BF16 if dtype == torch.bfloat16 else MOE_F32,
+                 ffn=MOE_FFN_SWIGLU if swiglu else MOE_FFN_SILU2, flags=flags, capacity=capacity)
+
+
+class Workspace:
+    """A device byte buffer that grows to what a shape needs and is then reused."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, shape: Shape) -> torch.Tensor:
+        n = _lib.workspace_size(shape)
+        if self.buf is None or self.buf.numel() < n:
+            self.buf = torch.empty(max(n, 256), dtype=torch.uint8,
+                                   device=self.device or torch.cuda.current_device())
+        return self.buf
+
+
+def forward(x, w_gate, w_in, w_up, w_out, top_k, bias=None, out=None, workspace=None,
+            flags=0, capacity_factor=None):
+    """The whole layer on the current stream; returns out [T, H] (x's dtype)."""
+    _need_cuda(x, w_gate, w_in, w_up, w_out, bias, out)
+    T, H = x.shape
+    E, _, F = w_in.shape
+    shape = Shape(T=T, H=H, E=E, k=top_k, F=F, dtype=_dtype_code(x),
+                  ffn=MOE_FFN_SWIGLU if w_up is not None else MOE_FFN_SILU2, flags=flags,
+                  capacity=capacity_rows(capacity_factor, T, top_k, E))
+    if out is None:
+        out = torch.empty_like(x)
+    ws = (workspace or Workspace(x.device)).get(shape)
+    _lib.forward(shape, x, w_gate, bias, w_in, w_up, w_out, out, ws)
+    return out
+
+
+def route(x, w_gate, top_k, bias=None, flags=0):
+    """Gate projection + top-k + gates: (logits [T,E] fp32, topk_idx [T,k] i32, topk_w [T,k] f32)."""
+    _need_cuda(x, w_gate, bias)
+    T, H = x.shape
+    E = w_gate.shape[1]
+    shape = Shape(T=T, H=H, E=E, k=top_k, F=8, dtype=_dtype_code(x), flags=flags)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    idx = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _lib.route(shape, x, w_gate, bias, logits, idx, w)
+    return logits, idx, w
+
+
+def route_from_logits(logits, top_k, bias=None, flags=0):
+    """Top-k + gates from given fp32 logits [T, E]: (topk_idx, topk_w)."""
+    _need_cuda(logits, bias)
+    T, E = logits.shape
+    shape = Shape(T=T, H=8, E=E, k=top_k, F=8, dtype=MOE_F32, flags=flags)
+    idx = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _lib.route(shape, None, None, bias, logits, idx, w)
+    return idx, w
+
+
+def permute(topk_idx, E, x=None, capacity=0, workspace=None, H=None, dtype=None):
+    """Group pairs by expert: dict(counts, offsets, sorted_token, row_of_pair, x_perm)."""
+    _need_cuda(topk_idx, x)
+    T, k = topk_idx.shape
+    if x is not None:
+        H, dtype = x.shape[1], x.dtype
+    H = H or 8
+    dtype = dtype or torch.bfloat16
+    shape = Shape(T=T, H=H, E=E, k=k, F=8, dtype=MOE_BF16 if dtype == torch.bfloat16 else MOE_F32,
+                  capacity=capacity)
+    dev = topk_idx.device
+    P = T * k
+    res = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_token=torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+               row_of_pair=torch.empty(max(P, 1), dtype=torch.int32, device=dev),
+               x_perm=None if x is None else torch.empty((max(P, 1), H), dtype=dtype, device=dev))
+    ws = (workspace or Workspace(dev)).get(shape)
+    _lib.permute(shape, topk_idx, x, res["counts"], res["offsets"], res["sorted_token"],
+                 res["row_of_pair"], res["x_perm"], ws)
+    return res
+
+
+def grouped_ffn(x_perm, offsets, w_in, w_up, w_out, top_k, T, workspace=None, y_perm=None):
+    """Grouped expert FFN over x_perm [T*k, H] -> y_perm [T*k, H]."""
+    _need_cuda(x_perm, offsets, w_in, w_up, w_out, y_perm)
+    E, H, F = w_in.shape
+    shape = Shape(T=T, H=H, E=E, k=top_k, F=F, dtype=_dtype_code(x_perm),
+                  ffn=MOE_FFN_SWIGLU if w_up is not None else MOE_FFN_SILU2)
+    if y_perm is None:
+        y_perm = torch.empty((max(T * top_k, 1), H), dtype=x_perm.dtype, device=x_perm.device)
+    ws = (workspace or Workspace(x_perm.device)).get(shape)
+    _lib.grouped_ffn(shape, x_perm, offsets, w_in, w_up, w_out, y_perm, ws)
+    return y_perm
+
+
+def combine(y_perm, row_of_pair, topk_w, out=None):
+    """out[t] = sum_j topk_w[t, j] * y_perm[row_of_pair[t*k + j]]."""
+    _need_cuda(y_perm, row_of_pair, topk_w, out)
+    T, k = topk_w.shape
+    H = y_perm.shape[1]
+    shape = Shape(T=T, H=H, E=max(k, 1), k=k, F=8, dtype=_dtype_code(y_perm))
+    if out is None:
+        out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    _lib.combine(shape, y_perm, row_of_pair, topk_w, out)
+    return out
+
+
+def router_stats(logits, counts, top_k, bias=None, offsets=None, capacity=0):
+    """Router monitoring statistics: (P [E], balance, entropy, top1_mean, drop_fraction)."""
+    _need_cuda(logits, counts, bias, offsets)
+    T, E = logits.shape
+    shape = Shape(T=T, H=8, E=E, k=top_k, F=8, dtype=MOE_F32, capacity=capacity)
+    stats = torch.empty(E + 4, dtype=torch.float32, device=logits.device)
+    _lib.router_stats(shape, logits, bias, counts, offsets, stats)
+    return stats

@@ -1,0 +1,182 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: tensors become device pointers, the current torch stream
+becomes the hipStream_t, and every step of the layer runs in the library's kernels.
+There is no fallback: if the library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_FFN_SILU2, MOE_FFN_SWIGLU = 0, 1
+MOE_FLAG_BIAS_SELECT_ONLY = 0x1
+MOE_FLAG_NO_RENORM = 0x2
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
+          4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
+
+EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
+           "moe_forward", "moe_router_stats", "moe_set_ffn_events", "moe_status_str",
+           "moe_last_error"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("flags", ctypes.c_uint32), ("capacity", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}: {detail}")
+        self.code = code
+        self.detail = detail
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m mixture_experts_layer_46_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    sp = ctypes.POINTER(MoeShape)
+    st = ctypes.c_void_p
+    sig = {
+        "moe_workspace_size": [sp, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_route": [sp, vp, f32p, f32p, f32p, i32p, f32p, st],
+        "moe_permute": [sp, i32p, vp, i32p, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, st],
+        "moe_grouped_ffn": [sp, vp, i32p, vp, vp, vp, vp, vp, ctypes.c_size_t, st],
+        "moe_combine": [sp, vp, i32p, f32p, vp, st],
+        "moe_forward": [sp, vp, f32p, f32p, vp, vp, vp, vp, vp, ctypes.c_size_t, st],
+        "moe_router_stats": [sp, f32p, f32p, i32p, i32p, f32p, st],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.moe_set_ffn_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_set_ffn_events.restype = ctypes.c_int
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise MoeError(fn, code, load().moe_last_error().decode())
+
+
+def capacity_rows(capacity_factor: float | None, T: int, k: int, E: int) -> int:
+    """Per-expert row limit C = ceil(cf * T * k / E) (0 = no limit)."""
+    if capacity_factor is None:
+        return 0
+    return max(1, int(math.ceil(capacity_factor * (T * k) / E)))
+
+
+@dataclass
+class Shape:
+    T: int
+    H: int
+    E: int
+    k: int
+    F: int
+    dtype: int = MOE_BF16
+    ffn: int = MOE_FFN_SWIGLU
+    flags: int = 0
+    capacity: int = 0
+
+    def c(self) -> MoeShape:
+        return MoeShape(self.T, self.H, self.E, self.k, self.F, self.dtype, self.ffn,
+                        self.flags, self.capacity)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    s = shape.c()
+    _check("moe_workspace_size", load().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)))
+    return n.value
+
+
+def route(shape: Shape, x, w_gate, bias, logits, topk_idx, topk_w, stream=None):
+    s = shape.c()
+    _check("moe_route", load().moe_route(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
+                                         _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                         _stream(stream)))
+
+
+def permute(shape: Shape, topk_idx, x, counts, offsets, sorted_token, row_of_pair, x_perm,
+            workspace, stream=None):
+    s = shape.c()
+    _check("moe_permute", load().moe_permute(ctypes.byref(s), _ptr(topk_idx), _ptr(x), _ptr(counts),
+                                             _ptr(offsets), _ptr(sorted_token), _ptr(row_of_pair),
+                                             _ptr(x_perm), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))
+
+
+def grouped_ffn(shape: Shape, x_perm, offsets, w_in, w_up, w_out, y_perm, workspace, stream=None):
+    s = shape.c()
+    _check("moe_grouped_ffn", load().moe_grouped_ffn(ctypes.byref(s), _ptr(x_perm), _ptr(offsets),
+                                                     _ptr(w_in), _ptr(w_up), _ptr(w_out),
+                                                     _ptr(y_perm), _ptr(workspace),
+                                                     workspace.numel() * workspace.element_size(),
+                                                     _stream(stream)))
+
+
+def combine(shape: Shape, y_perm, row_of_pair, topk_w, out, stream=None):
+    s = shape.c()
+    _check("moe_combine", load().moe_combine(ctypes.byref(s), _ptr(y_perm), _ptr(row_of_pair),
+                                             _ptr(topk_w), _ptr(out), _stream(stream)))
+
+
+def forward(shape: Shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, stream=None):
+    s = shape.c()
+    _check("moe_forward", load().moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
+                                             _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
+                                             _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))
+
+
+def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None):
+    s = shape.c()
+    _check("moe_router_stats", load().moe_router_stats(ctypes.byref(s), _ptr(logits), _ptr(bias),
+                                                       _ptr(counts), _ptr(offsets), _ptr(stats),
+                                                       _stream(stream)))
+
+
+def set_ffn_events(start=None, stop=None):
+    """Record torch.cuda.Event `start`/`stop` around the grouped FFN of later forward
+    calls on this thread (None, None switches it off)."""
+    a = None if start is None else start.cuda_event
+    b = None if stop is None else stop.cuda_event
+    _check("moe_set_ffn_events", load().moe_set_ffn_events(a, b))

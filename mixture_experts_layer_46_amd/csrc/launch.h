@@ -1,0 +1,59 @@
+// Host-side launchers of the MoE kernels (one per kernel family).  Each enqueues on
+// `st` and returns the launch status; shapes were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// pairs per segment of the grouping kernels (one wavefront handles one segment)
+constexpr int kSeg = 512;
+
+// One grouped-GEMM tile: rows [row0, row1) of expert `e` (row1 - row0 <= BM).
+struct Tile {
+    int e, row0, row1, pad;
+};
+
+// Tile configurations of the bf16 grouped GEMM.
+enum GemmCfg { GEMM_M16 = 0, GEMM_M64 = 1, GEMM_M128 = 2, GEMM_M256 = 3 };
+int gemm_cfg_bm(GemmCfg c);
+
+hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* logits,
+                              long long T, int H, int E, hipStream_t st);
+hipError_t launch_topk(const float* logits, const float* bias, int32_t* idx, float* w,
+                       long long T, int E, int k, unsigned flags, hipStream_t st);
+
+hipError_t launch_group(const int32_t* topk_idx, long long P, int k, int E, int capacity,
+                        int32_t* segcnt, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_token, int32_t* row_of_pair, hipStream_t st);
+hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                         int E, void* x_perm, long long P, int H, int esize, hipStream_t st);
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, Tile* tiles,
+                              int32_t* ntiles, hipStream_t st);
+
+// grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]].
+hipError_t launch_grouped_ffn_bf16(const void* a, const int32_t* gather_rows,
+                                   const void* w_in, const void* w_up, const void* w_out,
+                                   void* h, void* y, const Tile* tiles, const int32_t* ntiles,
+                                   long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
+                                   int gm, hipStream_t st);
+hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
+                                  const void* w_in, const void* w_up, const void* w_out,
+                                  void* h, void* y, const Tile* tiles, const int32_t* ntiles,
+                                  long long max_tiles, int H, int F, int swiglu,
+                                  hipStream_t st);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of_pair, const float* w,
+                          void* out, long long T, int k, int H, int dtype, hipStream_t st);
+
+hipError_t launch_router_stats(const float* logits, const float* bias, const int32_t* counts,
+                               const int32_t* offsets, float* stats, long long T, int E, int k,
+                               int capacity, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace moe

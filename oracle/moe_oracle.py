@@ -68,31 +68,36 @@ def select_topk(scores, k):
     return order[:, :k].astype(np.int32)
 
 
-def renormalised_gates(logits, idx):
+def renormalised_gates(logits, idx, renorm=True):
     """Softmax over all experts, then the selected probabilities divided by their
-    sum: g'_j = p_{e_j} / sum_j' p_{e_j'}.  [Principles §2.1, §2.2]"""
+    sum: g'_j = p_{e_j} / sum_j' p_{e_j'}.  [Principles §2.1, §2.2]
+    With renorm=False the selected probabilities are returned as they are, as in the
+    walk-through of [FourStage §3]."""
     p = softmax(logits)
     sel = np.take_along_axis(p, np.asarray(idx, np.int64), axis=-1)
-    return sel / sel.sum(axis=-1, keepdims=True)
+    return sel / sel.sum(axis=-1, keepdims=True) if renorm else sel
 
 
-def route(x, w_gate, bias, k):
-    """Full-precision routing from the hidden states: (logits, idx, gates)."""
-    l = gate_logits(x, w_gate, bias)
-    idx = select_topk(l, k)
-    return l, idx, renormalised_gates(l, idx)
+def route(x, w_gate, bias, k, select_only=False, renorm=True):
+    """Full-precision routing from the hidden states: (scores, idx, gates).
+    The ranking score is l + b.  With select_only the bias only picks the experts and
+    the gates come from the unbiased logits l ([Principles §4.4])."""
+    l = gate_logits(x, w_gate, None)
+    s = l if bias is None else l + np.asarray(bias, F64)[None, :]
+    idx = select_topk(s, k)
+    return s, idx, renormalised_gates(l if select_only else s, idx, renorm)
 
 
-def route_from_f32_logits(logits32, bias32, k):
+def route_from_f32_logits(logits32, bias32, k, select_only=False, renorm=True):
     """Routing from given fp32 logits, the way the bit-exact check feeds both sides:
     the biased score is one IEEE fp32 add, l' = fp32(L + b); the set is then chosen
-    on l' and the gates computed from l' in float64."""
-    l = np.asarray(logits32, np.float32)
+    on l' and the gates computed in float64 from l' (or from L with select_only)."""
+    L = np.asarray(logits32, np.float32)
+    l = L
     if bias32 is not None:
-        l = (l + np.asarray(bias32, np.float32)[None, :]).astype(np.float32)
-    l64 = l.astype(F64)
-    idx = select_topk(l64, k)
-    return l, idx, renormalised_gates(l64, idx)
+        l = (L + np.asarray(bias32, np.float32)[None, :]).astype(np.float32)
+    idx = select_topk(l.astype(F64), k)
+    return l, idx, renormalised_gates((L if select_only else l).astype(F64), idx, renorm)
 
 
 def topk_alternatives(logits_row, k, tol):
@@ -198,9 +203,11 @@ def combine(y_perm, row_of_pair, gates):
 
 # ------------------------------------------------------------------------- whole layer
 
-def forward(x, w_gate, bias, weights, k, ffn, capacity_factor=None):
+def forward(x, w_gate, bias, weights, k, ffn, capacity_factor=None, select_only=False,
+            renorm=True):
     """The layer forward on all tokens of x [T, H]; returns every intermediate.
 
+    ``logits`` in the result is the ranking score l + b.
     ``weights`` is (w_in, w_up, w_out) stacked over experts, or a callable that
     returns one expert's (w_in, w_up, w_out) -- so large layers can be streamed one
     expert at a time.  With ``capacity_factor`` the grouped rows of an expert beyond
@@ -208,7 +215,7 @@ def forward(x, w_gate, bias, weights, k, ffn, capacity_factor=None):
     ([Principles §4.3]; "total_tokens" read as token-expert pairs)."""
     x = np.asarray(x, F64)
     E = np.asarray(w_gate).shape[1]
-    logits, idx, gates = route(x, w_gate, bias, k)
+    logits, idx, gates = route(x, w_gate, bias, k, select_only, renorm)
     counts, offsets, sorted_token, row_of_pair = group_by_expert(idx, E)
     x_perm = x[sorted_token]
     y_perm = grouped_ffn(x_perm, offsets, weights, ffn)

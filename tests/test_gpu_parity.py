@@ -1,0 +1,261 @@
+"""GPU path vs the CPU oracle, stage by stage and end to end, at sizes the oracle
+finishes in seconds (several tiles plus ragged tails in every dimension).
+
+Bar: routing indices, counts, offsets, the permutation and x_perm bit-exact (fed
+identical fp32 logits / indices); gates within 1e-6; expert FFN and layer outputs
+within a normwise 1e-5 (fp32) or 2e-2 (bf16).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from workloads import MoEConfig, PRESETS, generate, to_numpy
+
+from gpu_util import (check_selection, gpu_inputs, normwise, run_forward, say, tol_for,
+                      weights_numpy)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import mixture_experts_layer_46_amd as M
+    from mixture_experts_layer_46_amd import _lib
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    _lib.load()          # fails loudly when the library is missing: no fallback
+    return M
+
+
+# --------------------------------------------------------------------------- routing
+
+ROUTE_CASES = [  # T, E, k, bias, flags
+    (300, 8, 2, False, 0), (257, 64, 2, True, 0), (129, 256, 8, True, 0), (64, 1, 1, False, 0),
+    (77, 5, 5, True, 0), (100, 100, 3, False, 0), (65, 256, 1, False, 0),
+    (90, 16, 4, True, 1), (90, 16, 4, True, 2), (90, 16, 4, True, 3),
+]
+
+
+@pytest.mark.parametrize("T,E,k,use_bias,flags", ROUTE_CASES)
+def test_route_from_logits_bit_exact(lib, T, E, k, use_bias, flags):
+    say(f"route_from_logits T={T} E={E} k={k} bias={use_bias} flags={flags}")
+    g = torch.Generator().manual_seed(1000 + T + E + k)
+    # quantised logits: many exact ties, and both signs of zero
+    L = torch.round(torch.randn(T, E, generator=g) * 3) / 4
+    L[::7, : min(E, 3)] = -0.0
+    L[::5, -1] = 0.0
+    L = L.float()
+    b = (torch.round(torch.randn(E, generator=g) * 2) / 8).float() if use_bias else None
+    idx, w = lib.route_from_logits(L.cuda(), k, bias=None if b is None else b.cuda(), flags=flags)
+    torch.cuda.synchronize()
+    _, ridx, rg = O.route_from_f32_logits(L.numpy(), None if b is None else b.numpy(), k,
+                                          select_only=bool(flags & 1), renorm=not (flags & 2))
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rg, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_from_x(lib, dtype):
+    cfg = MoEConfig("r", T=333, H=200, E=64, k=2, F=8, ffn="swiglu", dtype=dtype, bias="normal0.5")
+    say(f"route_from_x {cfg}")
+    d = generate(cfg, experts=False)
+    x, wg, b = d["x"].cuda(), d["w_gate"].cuda(), d["bias"].cuda()
+    logits, idx, w = lib.route(x, wg, cfg.k, bias=b)
+    torch.cuda.synchronize()
+    ref = O.gate_logits(to_numpy(d["x"]), to_numpy(d["w_gate"]))
+    got = logits.cpu().numpy().astype(np.float64)
+    assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+    scores, ridx, rg = O.route(to_numpy(d["x"]), to_numpy(d["w_gate"]), to_numpy(d["bias"]), cfg.k)
+    flips = check_selection(idx.cpu().numpy(), scores, cfg.k)
+    assert len(flips) <= 2
+    same = np.setdiff1d(np.arange(cfg.T), list(flips))
+    np.testing.assert_allclose(w.cpu().numpy()[same], rg[same], rtol=2e-5, atol=1e-6)
+
+
+# -------------------------------------------------------------------------- grouping
+
+PERMUTE_CASES = [  # T, E, k, H, capacity
+    (1, 4, 2, 64, 0), (37, 5, 2, 72, 0), (600, 8, 2, 128, 0), (1100, 64, 3, 40, 0),
+    (513, 256, 8, 16, 0), (700, 16, 4, 24, 0), (700, 16, 4, 24, 150), (300, 8, 2, 8, 40),
+]
+
+
+@pytest.mark.parametrize("T,E,k,H,cap", PERMUTE_CASES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_permute_bit_exact(lib, T, E, k, H, cap, dtype):
+    say(f"permute T={T} E={E} k={k} H={H} cap={cap} {dtype}")
+    g = torch.Generator().manual_seed(T * 31 + E)
+    # skewed distinct picks per token
+    w = torch.linspace(3.0, 0.1, E)
+    idx = torch.stack([torch.multinomial(w, k, replacement=False, generator=g) for _ in range(T)]).int()
+    x = torch.randn(T, H, generator=g).to(dtype)
+    r = lib.permute(idx.cuda(), E, x=x.cuda(), capacity=cap)
+    torch.cuda.synchronize()
+    counts, offsets, st, rop = O.group_by_expert(idx.numpy(), E)
+    assert np.array_equal(r["counts"].cpu().numpy(), counts)
+    if cap == 0:
+        assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+        P = T * k
+        assert np.array_equal(r["sorted_token"].cpu().numpy()[:P], st)
+        assert np.array_equal(r["row_of_pair"].cpu().numpy()[:P], rop)
+        assert torch.equal(r["x_perm"][:P].cpu(), x[torch.from_numpy(st).long()])
+    else:
+        kept = np.minimum(counts, cap)
+        offs = np.concatenate([[0], np.cumsum(kept)])
+        assert np.array_equal(r["offsets"].cpu().numpy(), offs)
+        # expected: the first `cap` pairs (token order) of each expert keep rows
+        want_rop = np.full(T * k, -1)
+        for e in range(E):
+            a, b = offsets[e], offsets[e + 1]
+            for i in range(min(cap, b - a)):
+                want_rop[st[a + i] * k + int(np.nonzero(idx.numpy()[st[a + i]] == e)[0][0])] = offs[e] + i
+        got_rop = r["row_of_pair"].cpu().numpy()[: T * k]
+        assert np.array_equal(got_rop, want_rop)
+        R = int(offs[-1])
+        got_st = r["sorted_token"].cpu().numpy()[:R]
+        for e in range(E):
+            assert np.array_equal(got_st[offs[e]:offs[e + 1]], st[offsets[e]:offsets[e] + kept[e]])
+
+
+# -------------------------------------------------------------------------- expert FFN
+
+FFN_CASES = [  # T, H, E, k, F, ffn, dtype  (mean rows per expert picks the row tile)
+    (256, 128, 8, 2, 256, "swiglu", "f32"), (37, 72, 5, 2, 40, "silu2", "f32"),
+    (24, 256, 16, 2, 512, "swiglu", "bf16"), (200, 200, 8, 2, 320, "silu2", "bf16"),
+    (512, 264, 4, 2, 136, "swiglu", "bf16"), (100, 128, 1, 1, 128, "silu2", "bf16"),
+    (300, 128, 256, 8, 64, "swiglu", "bf16"), (700, 192, 4, 2, 2056, "swiglu", "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,F,ffn,dtype", FFN_CASES)
+def test_grouped_ffn(lib, T, H, E, k, F, ffn, dtype):
+    cfg = MoEConfig("g", T=T, H=H, E=E, k=k, F=F, ffn=ffn, dtype=dtype, bias="none", seed=3)
+    say(f"grouped_ffn {cfg}")
+    d = generate(cfg)
+    g = torch.Generator().manual_seed(T + F)
+    idx = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).int().numpy()
+    counts, offsets, st, rop = O.group_by_expert(idx, E)
+    x_perm = d["x"][torch.from_numpy(st).long()]
+    y = lib.grouped_ffn(x_perm.cuda(), torch.from_numpy(offsets).cuda(), d["w_in"].cuda(),
+                        None if d["w_up"] is None else d["w_up"].cuda(), d["w_out"].cuda(), k, T)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(to_numpy(x_perm), offsets, weights_numpy(d), ffn)
+    err = normwise(to_numpy(y[: T * k]), ref)
+    say(f"  normwise error {err:.3e}")
+    assert err <= tol_for(cfg)
+
+
+# ---------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("T,k,H,dtype", [(1, 1, 8, torch.float32), (333, 2, 4096, torch.bfloat16),
+                                         (100, 8, 7168, torch.bfloat16), (50, 3, 120, torch.float32)])
+def test_combine(lib, T, k, H, dtype):
+    say(f"combine T={T} k={k} H={H} {dtype}")
+    g = torch.Generator().manual_seed(T * k)
+    P = T * k
+    y = torch.randn(P, H, generator=g).to(dtype)
+    rop = torch.randperm(P, generator=g).int()
+    rop[::5] = -1                                    # dropped pairs add nothing
+    w = torch.rand(T, k, generator=g)
+    out = lib.combine(y.cuda(), rop.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ynp = to_numpy(y)
+    ynp = np.concatenate([ynp, np.zeros((1, H))])    # row -1 -> zeros
+    ref = O.combine(ynp, np.where(rop.numpy() < 0, P, rop.numpy()), w.numpy().astype(np.float64))
+    tol = 1e-6 if dtype == torch.float32 else 8e-3
+    assert normwise(to_numpy(out), ref) <= tol
+
+
+# --------------------------------------------------------------------------- end to end
+
+E2E = [
+    PRESETS["tiny_f32"],
+    MoEConfig("f32_ragged", T=37, H=72, E=5, k=2, F=40, ffn="silu2", dtype="f32", bias="normal0.5"),
+    MoEConfig("decode_small", T=24, H=256, E=16, k=2, F=512, ffn="swiglu", dtype="bf16", bias="none"),
+    MoEConfig("mid_silu2", T=200, H=200, E=8, k=2, F=320, ffn="silu2", dtype="bf16", bias="none"),
+    MoEConfig("two_tiles", T=512, H=264, E=4, k=2, F=136, ffn="swiglu", dtype="bf16", bias="normal0.5"),
+    MoEConfig("k_eq_E", T=64, H=128, E=4, k=4, F=256, ffn="swiglu", dtype="bf16", bias="none"),
+    MoEConfig("one_expert", T=100, H=128, E=1, k=1, F=128, ffn="silu2", dtype="bf16", bias="none"),
+    MoEConfig("skew_256", T=300, H=128, E=256, k=8, F=64, ffn="swiglu", dtype="bf16", bias="zipf1.1"),
+    MoEConfig("one_token", T=1, H=64, E=8, k=2, F=64, ffn="swiglu", dtype="bf16", bias="none"),
+]
+
+
+def _oracle_forward(cfg, d, **kw):
+    return O.forward(to_numpy(d["x"]), to_numpy(d["w_gate"]), to_numpy(d["bias"]), weights_numpy(d),
+                     cfg.k, cfg.ffn, **kw)
+
+
+@pytest.mark.parametrize("cfg", E2E, ids=[c.name for c in E2E])
+def test_forward_matches_oracle(lib, cfg):
+    say(f"forward {cfg}")
+    d = generate(cfg)
+    inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    _, idx, _ = lib.route(inp["x"], inp["w_gate"], cfg.k, bias=inp["bias"])
+    out = run_forward(cfg, inp)
+    ref = _oracle_forward(cfg, d)
+    flips = check_selection(idx.cpu().numpy(), ref["logits"], cfg.k)
+    got = to_numpy(out)
+    keep = np.setdiff1d(np.arange(cfg.T), list(flips))
+    err = normwise(got[keep], ref["out"][keep])
+    say(f"  normwise error {err:.3e}, near-tie tokens {len(flips)}")
+    assert err <= tol_for(cfg)
+    for t, alt in flips.items():   # a near tie went the other way: output of that selection
+        want = O.token_output(to_numpy(d["x"])[t], ref["logits"][t], alt, weights_numpy(d), cfg.ffn)
+        assert normwise(got[t], want) <= tol_for(cfg)
+
+
+def test_forward_is_deterministic(lib):
+    cfg = MoEConfig("det", T=500, H=256, E=32, k=4, F=384, ffn="swiglu", dtype="bf16", bias="zipf1.1")
+    say(f"determinism {cfg}")
+    inp = gpu_inputs(cfg)
+    a = run_forward(cfg, inp).clone()
+    b = run_forward(cfg, inp)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cf", [0.5, 1.0])
+def test_forward_with_capacity(lib, cf):
+    cfg = MoEConfig("cap", T=300, H=128, E=8, k=2, F=192, ffn="swiglu", dtype="bf16", bias="normal0.5")
+    say(f"capacity cf={cf} {cfg}")
+    d = generate(cfg)
+    inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    out = run_forward(cfg, inp, capacity_factor=cf)
+    ref = _oracle_forward(cfg, d, capacity_factor=cf)
+    assert ref["keep"] is not None and not ref["keep"].all()
+    assert normwise(to_numpy(out), ref["out"]) <= tol_for(cfg)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_forward_routing_variants(lib, flags):
+    cfg = MoEConfig("var", T=200, H=128, E=16, k=3, F=128, ffn="silu2", dtype="f32", bias="normal0.5")
+    say(f"routing variant flags={flags}")
+    d = generate(cfg)
+    inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    out = run_forward(cfg, inp, flags=flags)
+    ref = _oracle_forward(cfg, d, select_only=bool(flags & 1), renorm=not (flags & 2))
+    assert normwise(to_numpy(out), ref["out"]) <= tol_for(cfg)
+
+
+def test_router_stats(lib):
+    cfg = MoEConfig("st", T=999, H=64, E=40, k=3, F=8, ffn="swiglu", dtype="f32", bias="normal0.5")
+    say("router stats")
+    d = generate(cfg, experts=False)
+    # both sides start from the same fp32 logits (made on the CPU)
+    L32 = O.gate_logits(to_numpy(d["x"]), to_numpy(d["w_gate"])).astype(np.float32)
+    b32 = d["bias"].numpy()
+    logits = torch.from_numpy(L32).cuda()
+    idx, _ = lib.route_from_logits(logits, cfg.k, bias=d["bias"].cuda())
+    r = lib.permute(idx, cfg.E)
+    s = lib.router_stats(logits, r["counts"], cfg.k, bias=d["bias"].cuda())
+    torch.cuda.synchronize()
+    s = s.cpu().numpy().astype(np.float64)
+    l, ridx, _ = O.route_from_f32_logits(L32, b32, cfg.k)
+    ref = O.router_stats(l.astype(np.float64), ridx, cfg.E)
+    np.testing.assert_allclose(s[:cfg.E], ref["P"], rtol=1e-4, atol=1e-7)
+    assert s[cfg.E] == pytest.approx(ref["balance"], rel=1e-4)
+    assert s[cfg.E + 1] == pytest.approx(ref["entropy"], rel=1e-4)
+    assert s[cfg.E + 2] == pytest.approx(ref["top1_mean"], rel=1e-4)
+    assert s[cfg.E + 3] == 0.0

@@ -345,7 +345,42 @@ def pin_alternatives():
     assert [a.tolist() for a in O.topk_alternatives(l, 2, 0.0)] == [[0, 3]]
 
 
-PINS = [pin_page_shapes, pin_topk_example, pin_weighted_output_example, pin_ties,
+def pin_no_renorm_example():
+    """Without renormalisation the gates are the raw top-k probabilities of the
+    walk-through example ([0.6, 0.2])."""
+    g = _gold("micro_examples.json")["topk_example"]
+    logits = np.log(np.array([g["probs"]]))
+    idx = O.select_topk(logits, g["k"])
+    np.testing.assert_allclose(O.renormalised_gates(logits, idx, renorm=False)[0], g["top_probs"],
+                               rtol=1e-12)
+    x = np.eye(4)[:1]
+    wg = np.zeros((4, 4))
+    wg[0] = logits[0]
+    _, idx2, g2 = O.route(x, wg, None, 2, renorm=False)
+    np.testing.assert_allclose(g2[0], g["top_probs"], rtol=1e-12)
+
+
+def pin_select_only_example():
+    """Bias only ranks: logits [2, 1, 0, -1] + bias [0, 0, 5, 0] pick experts 2 then 0;
+    the gates come from the unbiased logits 0 and 2: [1/(1+e^2), e^2/(1+e^2)]."""
+    x = np.eye(4)[:1]
+    wg = np.zeros((4, 4))                                   # x = e_0 reads row 0 of W_g
+    wg[0] = [2.0, 1.0, 0.0, -1.0]
+    b = np.array([0.0, 0.0, 5.0, 0.0])
+    s, idx, g = O.route(x, wg, b, 2, select_only=True)
+    assert idx[0].tolist() == [2, 0]
+    e2 = math.exp(2.0)
+    np.testing.assert_allclose(g[0], [1 / (1 + e2), e2 / (1 + e2)], rtol=1e-14)
+    s, idx, g = O.route(x, wg, b, 2)                        # gate bias: from l + b = [2, 5]
+    e3 = math.exp(3.0)
+    np.testing.assert_allclose(g[0], [e3 / (1 + e3), 1 / (1 + e3)], rtol=1e-14)
+    _, idx32, g32 = O.route_from_f32_logits(np.array([[2.0, 1.0, 0.0, -1.0]], np.float32),
+                                            b.astype(np.float32), 2, select_only=True)
+    assert idx32[0].tolist() == [2, 0]
+    np.testing.assert_allclose(g32[0], [1 / (1 + e2), e2 / (1 + e2)], rtol=1e-14)
+
+
+PINS = [pin_no_renorm_example, pin_select_only_example, pin_page_shapes, pin_topk_example, pin_weighted_output_example, pin_ties,
         pin_topk_bruteforce, pin_grouping_bruteforce, pin_layer_bruteforce, pin_k_equals_E,
         pin_single_expert_is_dense_ffn, pin_dense_masked_equals_grouped, pin_silu_closed_form,
         pin_selection_matrix_ffn, pin_f32_bias_add_is_one_rounding, pin_gate_invariants,
@@ -393,7 +428,7 @@ def _mut_drop_up(m):
 
 def _mut_no_renorm(m):
     m.setattr(O, "renormalised_gates",
-              lambda l, idx: np.take_along_axis(O.softmax(l), np.asarray(idx, np.int64), -1))
+              lambda l, idx, renorm=True: np.take_along_axis(O.softmax(l), np.asarray(idx, np.int64), -1))
 
 
 def _mut_smallest(m):
@@ -451,8 +486,8 @@ def _mut_transposed_down(m):
 
 
 def _mut_no_bias(m):
-    orig = O.gate_logits
-    m.setattr(O, "gate_logits", lambda x, w, b=None: orig(x, w, None))
+    orig = O.route
+    m.setattr(O, "route", lambda x, w, b, k, *a: orig(x, w, None, k, *a))
 
 
 def _mut_capacity_off_by_one(m):
@@ -461,12 +496,23 @@ def _mut_capacity_off_by_one(m):
 
 def _mut_gates_sign(m):
     orig = O.renormalised_gates
-    m.setattr(O, "renormalised_gates", lambda l, idx: orig(-np.asarray(l), idx))
+    m.setattr(O, "renormalised_gates", lambda l, idx, renorm=True: orig(-np.asarray(l), idx, renorm))
+
+
+def _mut_select_only_ignored(m):
+    orig = O.route
+    m.setattr(O, "route", lambda x, w, b, k, select_only=False, renorm=True: orig(x, w, b, k, False, renorm))
+
+
+def _mut_renorm_ignored(m):
+    orig = O.renormalised_gates
+    m.setattr(O, "renormalised_gates", lambda l, idx, renorm=True: orig(l, idx, True))
 
 
 MUTANTS = [_mut_silu_sigmoid, _mut_drop_up, _mut_no_renorm, _mut_smallest, _mut_tie_high,
            _mut_combine_wrong_index, _mut_unstable_group, _mut_transposed_down, _mut_no_bias,
-           _mut_capacity_off_by_one, _mut_gates_sign]
+           _mut_capacity_off_by_one, _mut_gates_sign, _mut_select_only_ignored,
+           _mut_renorm_ignored]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
