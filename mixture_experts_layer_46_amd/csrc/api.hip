@@ -121,7 +121,8 @@ GemmCfg pick_cfg(const moe_shape& s) {
     const double mean = (double)s.T * s.k / s.E;
     if (mean <= 24) return GEMM_M16;
     if (mean <= 80) return GEMM_M64;
-    return GEMM_M128;   // the 256-row tile is kept out until it fits without spills
+    if (mean <= 160) return GEMM_M128;
+    return GEMM_M256;
 }
 
 // Row tiles per super-group: row tiles of one expert that share a weight slice.
@@ -150,7 +151,7 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     const GemmCfg cfg = pick_cfg(s);
     const int BM = gemm_cfg_bm(cfg);
     HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
-    HIPCHK(launch_grouped_ffn_bf16(a, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
+    HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
                                    ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu,
                                    pick_gm(s, BM), st),
            "grouped_ffn_bf16");

@@ -244,6 +244,276 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     }
 }
 
+// --------------------------------------------- direct-to-LDS grouped GEMM (main path)
+// The grouped GEMM for row tiles of 64..256 rows.  Both operands travel from HBM
+// straight into LDS with buffer_load_dwordx4 ... lds (lane i's 16 bytes land in slot i
+// of the wavefront's 1 KB); a buffer resource bounds each operand, so chunks past K,
+// N or the tile's rows read as zeros and no register stages the tiles.
+//   * A (rows, k-contiguous): LDS [BM][32], chunk q of row m at q ^ ((m >> 2) & 3);
+//     fragments are ds_read_b128.
+//   * W (k rows, n-contiguous), kept as in memory: LDS [32][256] (SiLU2 and the second
+//     projection) or [2][32][128] (SwiGLU gate | up), 16-byte chunk c of row k at
+//     c ^ fk(k), fk(k) = 2 * ((k & 3) | ((k >> 3) & 1) << 2).  The MFMA operand (8
+//     consecutive k of one column per lane) comes from two ds_read_b64_tr_b16 (gfx950):
+//     within each group of 16 lanes, source lane j reads 4 consecutive columns of row
+//     k0 + j/4 and lane i receives column i of those four rows.  Both swizzles keep
+//     the lanes of one LDS cycle on distinct banks.
+//   * Four LDS stages of 32 k with the DMA three steps ahead.  One K step runs in a
+//     helper that takes the stage it reads and the stage it fills as separate
+//     __restrict__ pointers, so the compiler knows the fragment reads do not touch the
+//     buffer in flight and does not wait for it; the step's own wait is explicit
+//     (s_waitcnt vmcnt(<DMA issued after this stage>)).
+//   * 256 x 256 tile, 4 wavefronts of 128 x 128 (v_mfma_f32_16x16x32_bf16, fp32
+//     accumulators in AGPRs), which halves the bytes moved per FLOP against 128-row
+//     tiles; 128- and 64-row tiles use the same code with shorter wavefront tiles.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int fk(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+__device__ __forceinline__ int swa4(int m) { return (m >> 2) & 3; }
+
+constexpr uint32_t kOOB = 0x80000000u;          // an offset past every buffer: reads zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int NMAT>
+struct LdsShape {
+    static constexpr int BN = 256, BNm = BN / NMAT, WAVES_M = 2, WAVES_N = 2, BK = 32, NSTAGE = 4;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2, STAGE = A_STAGE + B_STAGE;
+    static constexpr int ADMA = A_STAGE / 1024 / 4;   // A DMA instructions per wavefront per step
+    static constexpr int BDMA = B_STAGE / 1024 / 4;   // W DMA instructions per wavefront per step
+    static constexpr int DPW = ADMA + BDMA;
+    static constexpr int BROW = 2 * BNm;              // LDS bytes per W row
+    static constexpr int CS_STRIDE = BNm + 8;
+    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
+                                            ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
+};
+
+// Per-tile DMA description (one wavefront's share of a K step).
+template <int ADMA, int BDMA>
+struct DmaPlan {                 // (the buffer resources travel as separate arguments)
+    uint32_t a_off[ADMA];        // byte offset of the lane's chunk at k0 = 0 (kOOB: none)
+    uint32_t a_k[ADMA];          // first k of the lane's chunk
+    uint32_t b_off[BDMA];        // byte offset at k0 = 0 (kOOB: column past N)
+};
+
+template <int BM, int NMAT>
+__device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                         __amdgpu_buffer_rsrc_t rb1,
+                                         const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                         int kt, int K, uint32_t rowB, int wave) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int ADMA = S::ADMA, BDMA = S::BDMA;
+    const uint32_t k0 = (uint32_t)kt * S::BK;
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i) {
+        const uint32_t off = (k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (wave * ADMA + i) * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < BDMA; ++i) {
+        const int j = wave * BDMA + i;
+        const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && j >= 8) ? rb1 : rb0,
+                                                 (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+// One K step: start the DMA of step kt_dma into `nxt` (if do_dma), then read this
+// step's fragments from `cur` and run its MFMAs.  `cur` and `nxt` are distinct stages;
+// saying so with __restrict__ lets the compiler issue the reads without waiting for
+// the DMA just started.
+template <int BM, int NMAT>
+__device__ __attribute__((always_inline)) inline void kstep(
+    const lds_char* __restrict__ cur, lds_char* __restrict__ nxt, bool do_dma, __amdgpu_buffer_rsrc_t ra,
+    __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int kt_dma, int K, uint32_t rowB,
+    int wave, int a_rd, int b_rd, int g, int wn,
+    f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
+    if (do_dma) dma_step<BM, NMAT>(nxt, ra, rb0, rb1, pl, kt_dma, K, rowB, wave);
+    const lds_char* As = cur;
+    const lds_char* Bs = cur + S::A_STAGE;
+    bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(As + a_rd + fm * 16 * S::BK * 2);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        int mat, blk;                          // W matrix and its 16-column block
+        if constexpr (NMAT == 1) {
+            mat = 0;
+            blk = wn * (S::WTN / 16) + fn;
+        } else {
+            mat = fn < FN / 2 ? 0 : 1;
+            blk = wn * (FN / 2) + (fn % (FN / 2));
+        }
+        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (((blk & ~7) | ((blk & 7) ^ g)) << 5);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bfr[fn] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+}
+
+// Wait until at most `pending` K steps' DMA of this wavefront are still in flight.
+template <int DPW>
+__device__ __forceinline__ void wait_dma(int pending) {
+    if (pending >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");
+    else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int BM, int NMAT, int ACT, bool GATHER>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N, int gm,
+    long long a_rows) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int BNm = S::BNm, WAVES_N = S::WAVES_N, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
+    constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, ADMA = S::ADMA, BDMA = S::BDMA;
+    constexpr int NSTAGE = S::NSTAGE, CS_STRIDE = S::CS_STRIDE, BROW = S::BROW;
+    static_assert(ADMA >= 1 && BDMA >= 1, "every wavefront moves part of each operand");
+    static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
+
+    extern __shared__ uint4 smem[];
+    lds_char* lds = (lds_char*)smem;
+    bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int l16 = lane & 15, lq = lane >> 4;
+
+    const int NT = (N + BNm - 1) / BNm;
+    const int KT = (K + BK - 1) / BK;
+    const int ntiles = *ntiles_p;
+    const long long total = (long long)ntiles * NT;
+    const int G = gridDim.x;
+    const long long first = (long long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t rowB = (uint32_t)N * 2;            // bytes per weight row in memory
+
+    // fragment read offsets: A row (wm*WTM + 16 fm + l16) chunk lq; W rows 8 lq + (l16 >> 2)
+    const int a_rd = (wm * WTM + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+    const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);             // fk(k) / 2 of this lane's rows
+    const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
+
+    for (long long w = first; w < total; w += G) {
+        const long long grp = w / ((long long)gm * NT);
+        const long long rem = w - grp * gm * NT;
+        const int gs = (int)min((long long)gm, (long long)ntiles - grp * gm);
+        const int nt = (int)(rem / gs);
+        const int mt = (int)(grp * gm + rem % gs);
+        const Tile tl = tiles[mt];
+        const int rows = tl.row1 - tl.row0;
+        const int n0 = nt * BNm;
+        const bool wave_rows = rows > wm * WTM;
+
+        DmaPlan<ADMA, BDMA> pl;
+        // A: instruction i of this wavefront covers 16 rows x 4 chunks; lane -> (row, chunk)
+#pragma unroll
+        for (int i = 0; i < ADMA; ++i) {
+            const int r = (wave * ADMA + i) * 16 + (lane >> 2);
+            const int q = (lane & 3) ^ swa4(r);
+            pl.a_k[i] = (uint32_t)(q * 8);
+            long long row = tl.row0 + min(r, rows - 1);
+            if constexpr (GATHER) row = gather_rows[row];
+            else row -= tl.row0;
+            pl.a_off[i] = (uint32_t)(row * K * 2) + (uint32_t)(q * 16);
+        }
+        const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, (uint32_t)(a_rows * K * 2))
+                                                 : make_rsrc(A + (long long)tl.row0 * K, (uint32_t)rows * K * 2);
+        const long long eoff = (long long)tl.e * K * N;
+        const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + eoff, (uint32_t)K * rowB);
+        const __amdgpu_buffer_rsrc_t rb1 = make_rsrc((NMAT == 2 ? B1 : B0) + eoff, (uint32_t)K * rowB);
+        // W: instruction j covers 2 rows x 32 chunks (SiLU2 / second projection) or
+        // 4 rows x 16 chunks of one matrix (SwiGLU)
+#pragma unroll
+        for (int i = 0; i < BDMA; ++i) {
+            const int j = wave * BDMA + i;
+            int k, c;
+            if constexpr (NMAT == 1) {
+                k = j * 2 + (lane >> 5);
+                c = (lane & 31) ^ fk(k);
+            } else {
+                k = (j & 7) * 4 + (lane >> 4);
+                c = (lane & 15) ^ fk(k);
+            }
+            const uint32_t col = (uint32_t)(n0 + 8 * c);
+            pl.b_off[i] = col < (uint32_t)N ? (uint32_t)k * rowB + col * 2 : kOOB;
+        }
+
+        f32x4_t acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // prologue: steps 0..NSTAGE-2 in flight
+        for (int t = 0; t < NSTAGE - 1 && t < KT; ++t)
+            dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
+        if (wave_rows) {
+            for (int kt = 0; kt < KT; ++kt) {
+                wait_dma<S::DPW>(min(kt + NSTAGE - 2, KT - 1) - kt);
+                __syncthreads();
+                kstep<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
+                                kt + NSTAGE - 1 < KT, ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd,
+                                b_rd, g, wn, acc);
+            }
+        } else {       // no rows for this wavefront: it still moves its share of the tiles
+            for (int kt = 0; kt < KT; ++kt) {
+                wait_dma<S::DPW>(min(kt + NSTAGE - 2, KT - 1) - kt);
+                __syncthreads();
+                if (kt + NSTAGE - 1 < KT)
+                    dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
+                                       kt + NSTAGE - 1, K, rowB, wave);
+            }
+        }
+        __syncthreads();
+
+        constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
+        if (wave_rows) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fo = 0; fo < FO; ++fo) {
+                    const int col = (NMAT == 2 ? wn * (BNm / WAVES_N) : wn * WTN) + 16 * fo + l16;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float val = acc[fm][fo][v];
+                        if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
+                        else if constexpr (ACT == 1) val = silu_f32(val);
+                        const int r = wm * WTM + 16 * fm + 4 * lq + v;
+                        sC[r * CS_STRIDE + col] = f32_to_bf16(val);
+                    }
+                }
+        }
+        __syncthreads();
+        constexpr int CPR = BNm / 8;
+        for (int c = tid; c < rows * CPR; c += 256) {
+            const int r = c / CPR, cc = c % CPR;
+            const int col = n0 + cc * 8;
+            if (col < N)
+                *reinterpret_cast<uint4*>(C + (long long)(tl.row0 + r) * N + col) =
+                    *reinterpret_cast<const uint4*>(sC + r * CS_STRIDE + cc * 8);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // stores out before the next DMA count
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------------------ tile list
 // One workgroup of 256 threads (E <= 256): expert e gets ceil(count_e / BM) tiles.
 __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__ offsets, int E,
@@ -288,66 +558,88 @@ int gemm_cfg_bm(GemmCfg c) {
 }
 
 // ------------------------------------------------------------------------ launching
-template <int BM, int NMAT, int WAVES_M, int ACT, bool GATHER>
-static hipError_t run_gemm(const void* A, const int32_t* gather_rows, const void* B0,
-                           const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
-                           long long max_items, int K, int N, int gm, hipStream_t st) {
-    using S = GemmShape<BM, 256, NMAT, WAVES_M>;
-    auto kern = k_grouped_gemm_bf16<BM, 256, NMAT, WAVES_M, ACT, GATHER>;
-    static bool attr_set = false;   // per process; the attribute is a property of the code object
-    if (!attr_set) {
+// Persistent grid: one workgroup per CU slot the kernel's LDS and registers allow,
+// rounded to a multiple of 8 (the XCD count) and capped by the work-item bound.
+template <typename KernT>
+static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int& occ_cache,
+                                  long long max_items, unsigned& grid) {
+    if (!ready) {   // per process: properties of the code object
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)S::LDS_BYTES);
+                                           (int)lds_bytes);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        int occ = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, lds_bytes) != hipSuccess || occ < 1)
+            occ = 1;
+        occ_cache = occ;
+        ready = true;
     }
-    int occ = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, S::LDS_BYTES) != hipSuccess || occ < 1)
-        occ = 1;
-    long long G = (long long)device_cu_count() * occ;
+    long long G = (long long)device_cu_count() * occ_cache;
     const long long cap = ((max_items + 7) / 8) * 8;
     if (G > cap) G = cap;
     G = ((G + 7) / 8) * 8;
     if (G < 8) G = 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(256), S::LDS_BYTES, st,
-                       (const bf16_t*)A, gather_rows, (const bf16_t*)B0, (const bf16_t*)B1,
-                       (bf16_t*)C, tiles, ntiles, K, N, gm);
+    grid = (unsigned)G;
+    return hipSuccess;
+}
+
+template <int BM, int NMAT, int WAVES_M, int ACT, bool GATHER>
+static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
+                           const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
+                           long long max_items, int K, int N, int gm, hipStream_t st) {
+    static bool ready = false;
+    static int occ = 1;
+    unsigned G = 0;
+    if constexpr (BM < 64) {
+        using S = GemmShape<BM, 256, NMAT, WAVES_M>;
+        auto kern = k_grouped_gemm_bf16<BM, 256, NMAT, WAVES_M, ACT, GATHER>;
+        hipError_t e = persistent_grid(kern, S::LDS_BYTES, ready, occ, max_items, G);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
+                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, gm);
+    } else {
+        using S = LdsShape<BM, NMAT>;
+        auto kern = k_grouped_gemm_lds<BM, NMAT, ACT, GATHER>;
+        hipError_t e = persistent_grid(kern, S::LDS_BYTES, ready, occ, max_items, G);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
+                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, gm, a_rows);
+    }
     return hipGetLastError();
 }
 
 template <int BM, int WAVES_M>
-static hipError_t run_ffn(const void* a, const int32_t* gather_rows, const void* w_in,
+static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather_rows, const void* w_in,
                           const void* w_up, const void* w_out, void* h, void* y,
                           const Tile* tiles, const int32_t* ntiles, long long max_tiles,
                           int H, int F, int swiglu, int gm, hipStream_t st) {
     hipError_t e;
     const long long items1 = max_tiles * ((F + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256));
     if (swiglu) {
-        e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st)
-                        : run_gemm<BM, 2, WAVES_M, 1, false>(a, nullptr, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st);
+        e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st)
+                        : run_gemm<BM, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st);
     } else {
-        e = gather_rows ? run_gemm<BM, 1, WAVES_M, 1, true>(a, gather_rows, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st)
-                        : run_gemm<BM, 1, WAVES_M, 1, false>(a, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st);
+        e = gather_rows ? run_gemm<BM, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st)
+                        : run_gemm<BM, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st);
     }
     if (e != hipSuccess) return e;
     const long long items2 = max_tiles * ((H + 255) / 256);
-    return run_gemm<BM, 1, WAVES_M, 0, false>(h, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, gm, st);
+    return run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, gm, st);
 }
 
-hipError_t launch_grouped_ffn_bf16(const void* a, const int32_t* gather_rows,
+hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_t* gather_rows,
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
                                    int gm, hipStream_t st) {
     switch (cfg) {
         case GEMM_M16:
-            return run_ffn<16, 1>(a, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
         case GEMM_M64:
-            return run_ffn<64, 1>(a, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
         case GEMM_M128:
-            return run_ffn<128, 2>(a, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
         default:
-            return run_ffn<256, 2>(a, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
     }
 }
 

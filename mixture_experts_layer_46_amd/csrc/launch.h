@@ -35,8 +35,10 @@ hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, Tile* tiles,
                               int32_t* ntiles, hipStream_t st);
 
-// grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]].
-hipError_t launch_grouped_ffn_bf16(const void* a, const int32_t* gather_rows,
+// grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]]
+// with x holding a_rows rows (its bytes must stay below 2^32 for the 32-bit buffer
+// offsets of the row-tile kernels).
+hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_t* gather_rows,
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
