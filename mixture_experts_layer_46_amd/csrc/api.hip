@@ -52,7 +52,7 @@ Layout layout_of(const moe_shape& s) {
     const size_t NS = (P + kSeg - 1) / kSeg;
     Layout L{};
     size_t o = 0;
-    L.logits = o;       o += up((size_t)s.T * s.E * 4);
+    L.logits = o;       o += up((size_t)gate_splits(s.T, s.H, s.E) * s.T * s.E * 4);
     L.topk_idx = o;     o += up(P * 4);
     L.topk_w = o;       o += up(P * 4);
     L.counts = o;       o += up((size_t)s.E * 4);
@@ -125,13 +125,6 @@ GemmCfg pick_cfg(const moe_shape& s) {
     return GEMM_M256;
 }
 
-// Row tiles per super-group: row tiles of one expert that share a weight slice.
-int pick_gm(const moe_shape& s, int BM) {
-    const double mean = (double)s.T * s.k / s.E;
-    int gm = (int)(mean / BM + 0.5);
-    return gm < 1 ? 1 : (gm > 8 ? 8 : gm);
-}
-
 moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_rows,
                        const int32_t* offsets, const void* w_in, const void* w_up,
                        const void* w_out, void* y, void* ws, hipStream_t st) {
@@ -152,8 +145,7 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     const int BM = gemm_cfg_bm(cfg);
     HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
-                                   ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu,
-                                   pick_gm(s, BM), st),
+                                   ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu, st),
            "grouped_ffn_bf16");
     return MOE_OK;
 }
@@ -203,10 +195,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
     REQ(topk_w, "topk_w");
     if (s.T == 0) return MOE_OK;
     (void)hipGetLastError();
-    if (x) {
-        HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, stream), "gate_logits");
-    }
-    HIPCHK(launch_topk(logits, bias, topk_idx, topk_w, s.T, s.E, s.k, s.flags, stream), "topk");
+    if (x) HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, 1, stream), "gate_logits");
+    HIPCHK(launch_topk(logits, 1, nullptr, bias, topk_idx, topk_w, s.T, s.E, s.k, s.flags, stream), "topk");
     return MOE_OK;
 }
 
@@ -298,8 +288,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     int32_t* offsets = at<int32_t>(workspace, L.offsets);
     int32_t* sorted_token = at<int32_t>(workspace, L.sorted_token);
     int32_t* row_of_pair = at<int32_t>(workspace, L.row_of_pair);
-    HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, stream), "gate_logits");
-    HIPCHK(launch_topk(logits, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");
+    const int splits = gate_splits(s.T, s.H, s.E);
+    HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, stream), "gate_logits");
+    HIPCHK(launch_topk(logits, splits, nullptr, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");
     HIPCHK(launch_group(idx, P, s.k, s.E, s.capacity, at<int32_t>(workspace, L.segcnt),
                         at<int32_t>(workspace, L.counts), offsets, sorted_token, row_of_pair, stream),
            "group");

@@ -27,8 +27,8 @@
 //     bank conflicts.
 //   * Rows past the expert's end skip their MFMAs (per 16-row block), so short
 //     experts cost little more than streaming their weights.
-//   * Work items are ordered (super-group of `gm` row tiles) x column block x row tile,
-//     and workgroup ids are remapped so that consecutive items run together on one XCD
+//   * Work items are ordered expert x column block x the expert's row tiles, and
+//     workgroup ids are remapped so that consecutive items run together on one XCD
 //     (ids are dealt round-robin to the 8 XCDs): row tiles that share a weight slice,
 //     and column blocks that share a row tile, meet in the same L2.
 //   * The epilogue applies SiLU / SwiGLU in fp32, rounds to bf16 once, stages the tile
@@ -62,7 +62,7 @@ template <int BM, int BN, int NMAT, int WAVES_M, int ACT, bool GATHER>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N, int gm) {
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N) {
     using S = GemmShape<BM, BN, NMAT, WAVES_M>;
     constexpr int WAVES_N = S::WAVES_N, BNm = S::BNm, WTM = S::WTM, FM = S::FM, FN = S::FN;
     constexpr int NA = S::NA, A_CHUNKS = S::A_CHUNKS;
@@ -107,11 +107,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 
     for (long long w = first; w < total; w += G) {
         // decode the work item
-        const long long grp = w / ((long long)gm * NT);
-        const long long rem = w - grp * gm * NT;
-        const int gs = (int)min((long long)gm, (long long)ntiles - grp * gm);
-        const int nt = (int)(rem / gs);
-        const int mt = (int)(grp * gm + rem % gs);
+        // items are expert-major, then column block, then the expert's row tiles, so all
+        // row tiles sharing one weight slice are consecutive (one XCD, one L2)
+        const Tile te = tiles[w / NT];
+        const long long local = w - (long long)te.first * NT;
+        const int nt = (int)(local / te.cnt);
+        const int mt = te.first + (int)(local % te.cnt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
@@ -379,7 +380,7 @@ template <int BM, int NMAT, int ACT, bool GATHER>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N, int gm,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
     long long a_rows) {
     using S = LdsShape<BM, NMAT>;
     constexpr int BNm = S::BNm, WAVES_N = S::WAVES_N, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
@@ -411,11 +412,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
 
     for (long long w = first; w < total; w += G) {
-        const long long grp = w / ((long long)gm * NT);
-        const long long rem = w - grp * gm * NT;
-        const int gs = (int)min((long long)gm, (long long)ntiles - grp * gm);
-        const int nt = (int)(rem / gs);
-        const int mt = (int)(grp * gm + rem % gs);
+        // items are expert-major, then column block, then the expert's row tiles, so all
+        // row tiles sharing one weight slice are consecutive (one XCD, one L2)
+        const Tile te = tiles[w / NT];
+        const long long local = w - (long long)te.first * NT;
+        const int nt = (int)(local / te.cnt);
+        const int mt = te.first + (int)(local % te.cnt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
     }
     const int incl = buf[cur][e];
     const int base = incl - nt;
-    for (int i = 0; i < nt; ++i) tiles[base + i] = Tile{e, r0 + i * BM, min(r0 + (i + 1) * BM, r1), 0};
+    for (int i = 0; i < nt; ++i) tiles[base + i] = Tile{e, r0 + i * BM, min(r0 + (i + 1) * BM, r1), base, nt, 0, 0, 0};
     if (e == 255) *ntiles = incl;
 }
 
@@ -585,7 +587,7 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
 template <int BM, int NMAT, int WAVES_M, int ACT, bool GATHER>
 static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
                            const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
-                           long long max_items, int K, int N, int gm, hipStream_t st) {
+                           long long max_items, int K, int N, hipStream_t st) {
     static bool ready = false;
     static int occ = 1;
     unsigned G = 0;
@@ -595,14 +597,14 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
         hipError_t e = persistent_grid(kern, S::LDS_BYTES, ready, occ, max_items, G);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
-                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, gm);
+                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N);
     } else {
         using S = LdsShape<BM, NMAT>;
         auto kern = k_grouped_gemm_lds<BM, NMAT, ACT, GATHER>;
         hipError_t e = persistent_grid(kern, S::LDS_BYTES, ready, occ, max_items, G);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
-                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, gm, a_rows);
+                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
     }
     return hipGetLastError();
 }
@@ -611,35 +613,35 @@ template <int BM, int WAVES_M>
 static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather_rows, const void* w_in,
                           const void* w_up, const void* w_out, void* h, void* y,
                           const Tile* tiles, const int32_t* ntiles, long long max_tiles,
-                          int H, int F, int swiglu, int gm, hipStream_t st) {
+                          int H, int F, int swiglu, hipStream_t st) {
     hipError_t e;
     const long long items1 = max_tiles * ((F + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256));
     if (swiglu) {
-        e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st)
-                        : run_gemm<BM, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items1, H, F, gm, st);
+        e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, st)
+                        : run_gemm<BM, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items1, H, F, st);
     } else {
-        e = gather_rows ? run_gemm<BM, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st)
-                        : run_gemm<BM, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, gm, st);
+        e = gather_rows ? run_gemm<BM, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items1, H, F, st)
+                        : run_gemm<BM, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, st);
     }
     if (e != hipSuccess) return e;
     const long long items2 = max_tiles * ((H + 255) / 256);
-    return run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, gm, st);
+    return run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, st);
 }
 
 hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_t* gather_rows,
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   int gm, hipStream_t st) {
+                                   hipStream_t st) {
     switch (cfg) {
         case GEMM_M16:
-            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
         case GEMM_M64:
-            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
         case GEMM_M128:
-            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
         default:
-            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, gm, st);
+            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
     }
 }
 

@@ -12,19 +12,25 @@ namespace moe {
 // pairs per segment of the grouping kernels (one wavefront handles one segment)
 constexpr int kSeg = 512;
 
-// One grouped-GEMM tile: rows [row0, row1) of expert `e` (row1 - row0 <= BM).
+// One grouped-GEMM row tile: rows [row0, row1) of expert `e` (row1 - row0 <= BM).  The
+// list is expert-major; `first` is the index of expert e's first tile and `cnt` its
+// number of tiles, so a work item can find its expert's tiles in O(1).
 struct Tile {
-    int e, row0, row1, pad;
+    int e, row0, row1, first, cnt, pad0, pad1, pad2;
 };
 
 // Tile configurations of the bf16 grouped GEMM.
 enum GemmCfg { GEMM_M16 = 0, GEMM_M64 = 1, GEMM_M128 = 2, GEMM_M256 = 3 };
 int gemm_cfg_bm(GemmCfg c);
 
-hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* logits,
-                              long long T, int H, int E, hipStream_t st);
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* idx, float* w,
-                       long long T, int E, int k, unsigned flags, hipStream_t st);
+// K splits of the gate projection (partial sums [splits][T][E]) for a layer shape
+int gate_splits(long long T, int H, int E);
+hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out,
+                              long long T, int H, int E, int splits, hipStream_t st);
+// top-k over the sum of `nparts` partial logits; the sum goes to logits_out if not NULL
+hipError_t launch_topk(const float* logits, int nparts, float* logits_out, const float* bias,
+                       int32_t* idx, float* w, long long T, int E, int k, unsigned flags,
+                       hipStream_t st);
 
 hipError_t launch_group(const int32_t* topk_idx, long long P, int k, int E, int capacity,
                         int32_t* segcnt, int32_t* counts, int32_t* offsets,
@@ -42,7 +48,7 @@ hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   int gm, hipStream_t st);
+                                   hipStream_t st);
 hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
                                   const void* w_in, const void* w_up, const void* w_out,
                                   void* h, void* y, const Tile* tiles, const int32_t* ntiles,

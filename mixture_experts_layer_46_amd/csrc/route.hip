@@ -17,64 +17,109 @@
 namespace moe {
 
 // ------------------------------------------------------------------ gate projection
-// Tile: GT_M tokens x 64 experts per workgroup, K step 32.  Wave w owns expert columns
-// [16w, 16w + 16) and all GT_M rows (GT_M / 16 MFMA blocks).
+// Tile: TM tokens x 64 experts per workgroup, K in steps of 64 over this workgroup's
+// K range (split-K: grid.z ranges, partial sums written per range and added in order
+// by the top-k kernel).  Wave w owns expert columns [16w, 16w + 16) and all TM rows.
+// The next step's x and W_g slabs are loaded into registers while the current step's
+// MFMAs run from LDS.
 constexpr int GT_E = 64;
-constexpr int GT_K = 32;
-constexpr int GT_PAD = 16;   // row pad (floats): lane groups of 16 land on distinct banks
+constexpr int GT_K = 64;
 
-template <int GT_M, typename XT>
+template <int TM, typename XT>
 __global__ __launch_bounds__(256) void k_gate_logits(const XT* __restrict__ x,
                                                      const float* __restrict__ wg,
-                                                     float* __restrict__ logits,
-                                                     int T, int H, int E) {
-    __shared__ float sA[GT_K][GT_M + GT_PAD];   // x tile, k-major
-    __shared__ float sB[GT_K][GT_E + GT_PAD];   // W_g tile
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m0 = blockIdx.x * GT_M, e0 = blockIdx.y * GT_E;
-    constexpr int FM = GT_M / 16;
+                                                     float* __restrict__ out, int T, int H, int E,
+                                                     int kchunk) {
+    __shared__ float sA[GT_K][TM + 16];     // x slab, k-major (fp32)
+    __shared__ float sB[GT_K][GT_E + 16];   // W_g slab
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m0 = blockIdx.x * TM, e0 = blockIdx.y * GT_E;
+    const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
+    constexpr int FM = TM / 16;
+    // x loader: thread -> (row m = tid % TM, 8-k chunk), TM*8 chunks of 8 per step
+    constexpr int XCH = TM * 8 / 256 > 0 ? TM * 8 / 256 : 1;   // chunks per thread
+    constexpr bool XPART = TM * 8 < 256;                        // some threads idle
+    const int xm = tid % TM, xc0 = tid / TM;
+    // W loader: thread -> (k row tid/16 + 16 j, 4 experts (tid % 16) * 4)
+    const int wk = tid >> 4, we = (tid & 15) * 4;
+    float xr[XCH][8];
+    float4 wr[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = xc0 + j * (256 / TM);
+            const int t = m0 + xm, kk = k0 + 8 * c;
+            const bool ok = (!XPART || tid < TM * 8) && t < T && kk < kend;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xr[j][i] = 0.f;
+            if (ok) {
+                if constexpr (sizeof(XT) == 4) {
+                    const float4 a = *reinterpret_cast<const float4*>(x + (size_t)t * H + kk);
+                    const float4 b = *reinterpret_cast<const float4*>(x + (size_t)t * H + kk + 4);
+                    xr[j][0] = a.x; xr[j][1] = a.y; xr[j][2] = a.z; xr[j][3] = a.w;
+                    xr[j][4] = b.x; xr[j][5] = b.y; xr[j][6] = b.z; xr[j][7] = b.w;
+                } else {
+                    const uint4 q = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+                    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xr[j][2 * i] = bf16lo_to_f32(d[i]);
+                        xr[j][2 * i + 1] = bf16hi_to_f32(d[i]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = k0 + wk + 16 * j, e = e0 + we;
+            wr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kk < kend) {
+                if (e + 3 < E) {
+                    wr[j] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
+                } else {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = (e + i < E) ? wg[(size_t)kk * E + e + i] : 0.f;
+                    wr[j] = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = xc0 + j * (256 / TM);
+            if (!XPART || tid < TM * 8)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sA[8 * c + i][xm] = xr[j][i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(&sB[wk + 16 * j][we]) = wr[j];
+    };
     f32x4_t acc[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < H; k0 += GT_K) {
-        // x tile: GT_M rows x 32 k, converted to fp32, stored transposed.
-        for (int c = tid; c < GT_M * (GT_K / 4); c += 256) {
-            const int r = c / (GT_K / 4), kq = (c % (GT_K / 4)) * 4;
-            const int t = m0 + r, kk = k0 + kq;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (t < T && kk < H) {   // H % 8 == 0, so a group of 4 never straddles H
-                if constexpr (sizeof(XT) == 4) {
-                    const float4 q = *reinterpret_cast<const float4*>(x + (size_t)t * H + kk);
-                    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-                } else {
-                    const uint2 q = *reinterpret_cast<const uint2*>(x + (size_t)t * H + kk);
-                    v[0] = bf16lo_to_f32(q.x); v[1] = bf16hi_to_f32(q.x);
-                    v[2] = bf16lo_to_f32(q.y); v[3] = bf16hi_to_f32(q.y);
+    if (kbeg < kend) {
+        gload(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (k0 + GT_K < kend) gload(k0 + GT_K);
+#pragma unroll
+            for (int ks = 0; ks < GT_K; ks += 4) {
+                const float bv = sB[ks + (lane >> 4)][wave * 16 + (lane & 15)];
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const float av = sA[ks + (lane >> 4)][fm * 16 + (lane & 15)];
+                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[fm], 0, 0, 0);
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sA[kq + i][r] = v[i];
         }
-        // W_g tile: 32 k x 64 experts (E may be smaller: zero-fill).
-        for (int c = tid; c < GT_K * GT_E; c += 256) {
-            const int kr = c / GT_E, ec = c % GT_E;
-            const int kk = k0 + kr, e = e0 + ec;
-            sB[kr][ec] = (kk < H && e < E) ? wg[(size_t)kk * E + e] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < GT_K; ks += 4) {
-            const float b = sB[ks + (lane >> 4)][wave * 16 + (lane & 15)];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const float a = sA[ks + (lane >> 4)][fm * 16 + (lane & 15)];
-                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[fm], 0, 0, 0);
-            }
-        }
-        __syncthreads();
     }
     // 16x16 fp32 block: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
+    float* o = out + (size_t)blockIdx.z * T * E;
     const int e = e0 + wave * 16 + (lane & 15);
     if (e < E) {
 #pragma unroll
@@ -82,7 +127,7 @@ __global__ __launch_bounds__(256) void k_gate_logits(const XT* __restrict__ x,
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = m0 + fm * 16 + 4 * (lane >> 4) + v;
-                if (t < T) logits[(size_t)t * E + e] = acc[fm][v];
+                if (t < T) o[(size_t)t * E + e] = acc[fm][v];
             }
     }
 }
@@ -123,7 +168,10 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // One wavefront per token, four tokens per workgroup.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
+// `logits` holds `nparts` partial sums [nparts][T][E] (split K); they are added in
+// order and, when `logits_out` is given, the sum is written there.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nparts,
+                                              float* __restrict__ logits_out,
                                               const float* __restrict__ bias,
                                               int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w,
@@ -139,7 +187,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
         live[q] = e < E;
-        const float l = live[q] ? logits[t * E + e] : 0.f;
+        float l = 0.f;
+        if (live[q]) {
+            l = logits[t * E + e];
+            for (int p = 1; p < nparts; ++p) l += logits[(long long)p * T * E + t * E + e];
+            if (logits_out) logits_out[t * E + e] = l;
+        }
         const float b = (live[q] && bias) ? bias[e] : 0.f;
         s[q] = l + b;                       // one fp32 add: the ranking score
         g[q] = select_only ? l : s[q];      // what the gate is computed from
@@ -202,34 +255,40 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
 }
 
 // -------------------------------------------------------------------- launchers
-hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* logits,
-                              long long T, int H, int E, hipStream_t st) {
+int gate_splits(long long T, int H, int E) {
+    const long long tm = T <= 256 ? 16 : 64;
+    const long long base = ((T + tm - 1) / tm) * ((E + GT_E - 1) / GT_E);
+    long long sp = (512 + base - 1) / base;
+    const long long maxs = (H + 255) / 256;
+    if (sp > maxs) sp = maxs;
+    return (int)(sp < 1 ? 1 : sp);
+}
+
+hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out, long long T, int H,
+                              int E, int splits, hipStream_t st) {
     const dim3 blk(256);
-    // 32-token tiles when E fits one 64-expert tile (more workgroups), else 64.
-    if (E <= GT_E) {
-        const dim3 grid((unsigned)((T + 31) / 32), 1);
+    const int kchunk = ((H + splits - 1) / splits + GT_K - 1) / GT_K * GT_K;
+    const unsigned gy = (unsigned)((E + GT_E - 1) / GT_E);
+    if (T <= 256) {
+        const dim3 grid((unsigned)((T + 15) / 16), gy, (unsigned)splits);
         if (dtype == MOE_F32)
-            hipLaunchKernelGGL((k_gate_logits<32, float>), grid, blk, 0, st,
-                               (const float*)x, wg, logits, (int)T, H, E);
+            hipLaunchKernelGGL((k_gate_logits<16, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
         else
-            hipLaunchKernelGGL((k_gate_logits<32, bf16_t>), grid, blk, 0, st,
-                               (const bf16_t*)x, wg, logits, (int)T, H, E);
+            hipLaunchKernelGGL((k_gate_logits<16, bf16_t>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
     } else {
-        const dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + GT_E - 1) / GT_E));
+        const dim3 grid((unsigned)((T + 63) / 64), gy, (unsigned)splits);
         if (dtype == MOE_F32)
-            hipLaunchKernelGGL((k_gate_logits<64, float>), grid, blk, 0, st,
-                               (const float*)x, wg, logits, (int)T, H, E);
+            hipLaunchKernelGGL((k_gate_logits<64, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
         else
-            hipLaunchKernelGGL((k_gate_logits<64, bf16_t>), grid, blk, 0, st,
-                               (const bf16_t*)x, wg, logits, (int)T, H, E);
+            hipLaunchKernelGGL((k_gate_logits<64, bf16_t>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* idx, float* w,
-                       long long T, int E, int k, unsigned flags, hipStream_t st) {
+hipError_t launch_topk(const float* logits, int nparts, float* logits_out, const float* bias, int32_t* idx,
+                       float* w, long long T, int E, int k, unsigned flags, hipStream_t st) {
     hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st,
-                       logits, bias, idx, w, T, E, k, flags);
+                       logits, nparts, logits_out, bias, idx, w, T, E, k, flags);
     return hipGetLastError();
 }
 
