@@ -7,9 +7,10 @@ FFN, combine) over one batch of synthetic inputs resident in HBM.  The default
 workload is the pages' worked shape: 8192 tokens (batch 4 x seq 2048), hidden 4096,
 64 experts, top-2, two-layer SiLU FFN 4096 -> 16384 -> 4096, bf16 with fp32 routing.
 
-Prints one JSON line: tokens/s, the grouped expert FFN's roofline figures (timed live
-with HIP events that moe_forward records around that phase on its stream) and the
-CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s, the roofline figures of the dominant grouped-GEMM kernel
+(timed live with HIP events that moe_forward records around each projection's launch on
+its stream; the other projection is reported beside it) and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="pages_worked_shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32,
+    ap.add_argument("--cpu-tokens", type=int, default=128,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
@@ -68,8 +69,9 @@ def main():
     torch.cuda.synchronize()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
@@ -88,10 +90,10 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for s0, s1 in ev:            # materialise the event handles
-        s0.record()
-        s1.record()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
+    for trio in ev:              # materialise the event handles
+        for e in trio:
+            e.record()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -100,34 +102,37 @@ def main():
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.set_ffn_events(None, None)
+    _lib.set_ffn_events()
 
     ms_step = (t1 - t0) * 1e3 / K
-    ffn_ms = float(np.mean([a.elapsed_time(c) for a, c in ev]))
+    up_ms = float(np.mean([a.elapsed_time(m) for a, m, _ in ev]))
+    down_ms = float(np.mean([m.elapsed_time(c) for _, m, c in ev]))
+    ffn_ms = up_ms + down_ms
     tokens_per_s = cfg.T * K / (t1 - t0)
 
-    eb = A.elem_bytes(cfg.dtype)
-    P = cfg.T * cfg.k
+    sb = A.stage_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.ffn, cfg.dtype, touched)
     flops = A.ffn_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn)
-    wbytes = touched * A.expert_weight_bytes(cfg.H, cfg.F, cfg.ffn, cfg.dtype)
-    ffn_bytes = wbytes + cfg.T * cfg.H * eb + P * cfg.H * eb
     peak_flops = A.PEAK_BF16_FLOPS if cfg.dtype == "bf16" else A.PEAK_FP32_FLOPS
-    t_mfma = flops / peak_flops
-    t_hbm = ffn_bytes / A.PEAK_HBM_BPS
+    kernels = {
+        "up": dict(name=_gemm_kernel_name(cfg, up=True), ms=up_ms,
+                   flops=A.ffn_up_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn), bytes=sb.ffn_up),
+        "down": dict(name=_gemm_kernel_name(cfg, up=False), ms=down_ms,
+                     flops=A.ffn_down_flops(cfg.T, cfg.k, cfg.H, cfg.F), bytes=sb.ffn_down),
+    }
+    for kd in kernels.values():
+        kd["roofline"] = _roofline(kd, peak_flops)
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    roof = dict(kernels[dom]["roofline"])
+    roof["traffic"] = _traffic(cfg.name, dom, kernels[dom]["name"])
+    roof["kernel"] = kernels[dom]["name"]
+    roof["ms"] = kernels[dom]["ms"]
+    roof["algorithmic_bytes"] = kernels[dom]["bytes"]
+    roof["algorithmic_flops"] = kernels[dom]["flops"]
+    other = "down" if dom == "up" else "up"
+    roof["other_projection"] = dict(kernels[other]["roofline"], kernel=kernels[other]["name"],
+                                    ms=kernels[other]["ms"])
+    t_ffn_roof = max(flops / peak_flops, (sb.ffn_up + sb.ffn_down) / A.PEAK_HBM_BPS)
     sec = ffn_ms * 1e-3
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": ffn_bytes / sec / 1e9, "peak": A.PEAK_HBM_BPS / 1e9,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": peak_flops / 1e12,
-                "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped expert FFN (tile list + both k_grouped_gemm_bf16 projections)"
-    roof["ms"] = ffn_ms
-    roof["algorithmic_bytes"] = ffn_bytes
-    roof["algorithmic_flops"] = flops
-    roof["roofline_ms"] = max(t_mfma, t_hbm) * 1e3
 
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -139,6 +144,8 @@ def main():
                    "ffn": cfg.ffn, "bias": cfg.bias, "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
         "grouped_gemm_tflops": flops / sec / 1e12,
         "grouped_gemm_pct_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS * 100,
+        "grouped_ffn_ms": ffn_ms,
+        "grouped_ffn_pct_roofline": t_ffn_roof / sec * 100,
         "touched_experts": touched,
         "roofline": roof,
         "cpu_baseline": None,
@@ -147,6 +154,63 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _gemm_kernel_name(cfg, up: bool) -> str:
+    """Name of the grouped-GEMM kernel a projection launches (as rocprofv3 lists it); the
+    tile height follows the library's choice from the mean rows per expert."""
+    if cfg.dtype != "bf16":
+        return "k_grouped_gemm_f32<%d, %d, %s>" % ((2 if cfg.ffn == "swiglu" else 1) if up else 1,
+                                                    1 if up else 0, "true" if up else "false")
+    mean = cfg.T * cfg.k / cfg.E
+    bm = 16 if mean <= 24 else 64 if mean <= 80 else 128 if mean <= 160 else 256
+    nmat = (2 if cfg.ffn == "swiglu" else 1) if up else 1
+    if bm == 16:
+        return "k_grouped_gemm_bf16<16, 256, %d, 1, %d, %s>" % (nmat, 1 if up else 0,
+                                                               "true" if up else "false")
+    return "k_grouped_gemm_lds<%d, %d, %d, %s>" % (bm, nmat, 1 if up else 0, "true" if up else "false")
+
+
+def _roofline(kd, peak_flops):
+    """Roofline figures of one kernel from its algorithmic flops/bytes and its mean time."""
+    import mixture_experts_layer_46_amd.accounting as A
+    sec = kd["ms"] * 1e-3
+    t_mfma = kd["flops"] / peak_flops
+    t_hbm = kd["bytes"] / A.PEAK_HBM_BPS
+    if t_hbm >= t_mfma:
+        r = {"bound": "hbm", "achieved": kd["bytes"] / sec / 1e9, "peak": A.PEAK_HBM_BPS / 1e9,
+             "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": kd["flops"] / sec / 1e12, "peak": peak_flops / 1e12,
+             "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["roofline_ms"] = max(t_mfma, t_hbm) * 1e3
+    return r
+
+
+def _traffic(workload: str, which: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when there is no
+    summary or the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "mixture_experts_layer_46_amd", "csrc", "grouped_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("grouped_gemm.hip sha256") != digest:
+        return None
+    if fields.get(f"{which} kernel") != kernel:
+        return None
+    try:
+        return float(fields[f"{which} hbm bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, inp, n_tokens):

@@ -171,12 +171,14 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
                             const int32_t* counts, const int32_t* offsets, float* stats,
                             hipStream_t stream);
 
-/* Timing hook for benchmarks.  When both events are non-NULL, later moe_forward calls
- * made by the calling thread record `start` on their stream just before the grouped
- * expert FFN (tile list + both projections) and `stop` just after it, so the caller
- * can read that phase's duration with hipEventElapsedTime.  The events are the
- * caller's (created with timing enabled); NULL, NULL switches the hook off.  Host only. */
-moe_status moe_set_ffn_events(hipEvent_t start, hipEvent_t stop);
+/* Timing hook for benchmarks.  When all three events are non-NULL, later moe_forward
+ * calls made by the calling thread record, on their stream, `up_start` just before the
+ * launch of the first expert projection (w_in, and w_up for SwiGLU), `mid` between it and
+ * the launch of the second projection (w_out), and `down_stop` just after that one, so
+ * the caller can read each projection kernel's duration with hipEventElapsedTime.  The
+ * events are the caller's (created with timing enabled); all NULL switches the hook off,
+ * a mix of NULL and non-NULL is MOE_ERR_NULL.  Host only. */
+moe_status moe_set_ffn_events(hipEvent_t up_start, hipEvent_t mid, hipEvent_t down_stop);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);

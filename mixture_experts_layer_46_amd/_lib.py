@@ -68,7 +68,7 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.moe_set_ffn_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_set_ffn_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_set_ffn_events.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -174,9 +174,9 @@ def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None
                                                        _stream(stream)))
 
 
-def set_ffn_events(start=None, stop=None):
-    """Record torch.cuda.Event `start`/`stop` around the grouped FFN of later forward
-    calls on this thread (None, None switches it off)."""
-    a = None if start is None else start.cuda_event
-    b = None if stop is None else stop.cuda_event
-    _check("moe_set_ffn_events", load().moe_set_ffn_events(a, b))
+def set_ffn_events(up_start=None, mid=None, down_stop=None):
+    """Record torch.cuda.Event objects before the first expert projection, between the
+    two projections and after the second, in later forward calls on this thread (no
+    arguments switches it off)."""
+    ev = [None if e is None else e.cuda_event for e in (up_start, mid, down_stop)]
+    _check("moe_set_ffn_events", load().moe_set_ffn_events(*ev))

@@ -39,6 +39,16 @@ def ffn_flops(T: int, k: int, H: int, F: int, ffn: str) -> int:
     return T * k * ffn_flops_per_pair(H, F, ffn)
 
 
+def ffn_up_flops(T: int, k: int, H: int, F: int, ffn: str) -> int:
+    """FLOPs of the first grouped projection (W_in, and W_up for SwiGLU)."""
+    return T * k * (n_mats(ffn) - 1) * 2 * H * F
+
+
+def ffn_down_flops(T: int, k: int, H: int, F: int) -> int:
+    """FLOPs of the second grouped projection (W_out)."""
+    return T * k * 2 * F * H
+
+
 def gate_flops(T: int, H: int, E: int) -> int:
     return 2 * T * H * E
 
@@ -52,7 +62,7 @@ class StageBytes:
     """Algorithmic HBM bytes of each stage, given the number of experts touched."""
     route: int
     permute: int
-    ffn_up: int        # first grouped GEMM: touched W_in (+W_up) + x rows in + h out
+    ffn_up: int        # first grouped GEMM: touched W_in (+W_up) + x once + h out
     ffn_down: int      # second grouped GEMM: touched W_out + h in + y rows out
     combine: int
     layer: int         # the whole layer: touched weights once + x in + out
@@ -66,7 +76,7 @@ def stage_bytes(T: int, H: int, E: int, k: int, F: int, ffn: str, dtype: str,
     permute = T * H * b + P * H * b + P * 16
     w_up_side = (n_mats(ffn) - 1) * H * F * b * touched
     w_down_side = F * H * b * touched
-    ffn_up = w_up_side + P * H * b + P * F * b
+    ffn_up = w_up_side + T * H * b + P * F * b      # rows are gathered from x itself
     ffn_down = w_down_side + P * F * b + P * H * b
     combine = P * H * b + T * H * b + P * 8
     layer = w_up_side + w_down_side + 2 * T * H * b

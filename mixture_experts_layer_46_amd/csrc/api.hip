@@ -15,7 +15,8 @@ namespace moe {
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_ffn_start = nullptr, g_ffn_stop = nullptr;
+// timing hook of moe_set_ffn_events: {before up, between, after down}, or all NULL
+thread_local hipEvent_t g_ffn_ev[3] = {nullptr, nullptr, nullptr};
 
 moe_status fail(moe_status st, const char* fmt, ...) {
     char buf[512];
@@ -127,7 +128,8 @@ GemmCfg pick_cfg(const moe_shape& s) {
 
 moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_rows,
                        const int32_t* offsets, const void* w_in, const void* w_up,
-                       const void* w_out, void* y, void* ws, hipStream_t st) {
+                       const void* w_out, void* y, void* ws, const hipEvent_t* ev,
+                       hipStream_t st) {
     const Layout L = layout_of(s);
     const long long P = s.T * (long long)s.k;
     const int swiglu = s.ffn == MOE_FFN_SWIGLU;
@@ -137,7 +139,7 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
         const int BM = 64;
         HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
         HIPCHK(launch_grouped_ffn_f32(a, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
-                                      ntiles, max_tiles_for(P, s.E, BM), s.H, s.F, swiglu, st),
+                                      ntiles, max_tiles_for(P, s.E, BM), s.H, s.F, swiglu, ev, st),
                "grouped_ffn_f32");
         return MOE_OK;
     }
@@ -145,7 +147,7 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     const int BM = gemm_cfg_bm(cfg);
     HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
-                                   ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu, st),
+                                   ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu, ev, st),
            "grouped_ffn_bf16");
     return MOE_OK;
 }
@@ -245,7 +247,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int
     if ((st = check_ws(s, workspace, ws_bytes)) != MOE_OK) return st;
     if (s.T == 0) return MOE_OK;
     (void)hipGetLastError();
-    return run_grouped(s, x_perm, nullptr, offsets, w_in, w_up, w_out, y_perm, workspace, stream);
+    return run_grouped(s, x_perm, nullptr, offsets, w_in, w_up, w_out, y_perm, workspace, nullptr, stream);
 }
 
 moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* row_of_pair,
@@ -295,11 +297,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
                         at<int32_t>(workspace, L.counts), offsets, sorted_token, row_of_pair, stream),
            "group");
     // the first projection reads x rows through sorted_token: no x_perm copy
-    if (g_ffn_start) HIPCHK(hipEventRecord(g_ffn_start, stream), "ffn start event");
     st = run_grouped(s, x, sorted_token, offsets, w_in, w_up, w_out, at<void>(workspace, L.y),
-                     workspace, stream);
+                     workspace, g_ffn_ev[0] ? g_ffn_ev : nullptr, stream);
     if (st != MOE_OK) return st;
-    if (g_ffn_stop) HIPCHK(hipEventRecord(g_ffn_stop, stream), "ffn stop event");
     HIPCHK(launch_combine(at<void>(workspace, L.y), row_of_pair, gw, out, s.T, s.k, s.H, s.dtype, stream),
            "combine");
     return MOE_OK;
@@ -324,10 +324,12 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
     return MOE_OK;
 }
 
-moe_status moe_set_ffn_events(hipEvent_t start, hipEvent_t stop) {
-    if ((start == nullptr) != (stop == nullptr)) return fail(MOE_ERR_NULL, "give both events or neither");
-    g_ffn_start = start;
-    g_ffn_stop = stop;
+moe_status moe_set_ffn_events(hipEvent_t up_start, hipEvent_t mid, hipEvent_t down_stop) {
+    const int given = (up_start != nullptr) + (mid != nullptr) + (down_stop != nullptr);
+    if (given != 0 && given != 3) return fail(MOE_ERR_NULL, "give all three events or none");
+    g_ffn_ev[0] = up_start;
+    g_ffn_ev[1] = mid;
+    g_ffn_ev[2] = down_stop;
     return MOE_OK;
 }
 

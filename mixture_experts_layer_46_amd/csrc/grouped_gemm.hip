@@ -613,8 +613,9 @@ template <int BM, int WAVES_M>
 static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather_rows, const void* w_in,
                           const void* w_up, const void* w_out, void* h, void* y,
                           const Tile* tiles, const int32_t* ntiles, long long max_tiles,
-                          int H, int F, int swiglu, hipStream_t st) {
+                          int H, int F, int swiglu, const hipEvent_t* ev, hipStream_t st) {
     hipError_t e;
+    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
     const long long items1 = max_tiles * ((F + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256));
     if (swiglu) {
         e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, st)
@@ -624,24 +625,27 @@ static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather
                         : run_gemm<BM, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, st);
     }
     if (e != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const long long items2 = max_tiles * ((H + 255) / 256);
-    return run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, st);
+    e = run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, st);
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+    return e;
 }
 
 hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_t* gather_rows,
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   hipStream_t st) {
+                                   const hipEvent_t* ev, hipStream_t st) {
     switch (cfg) {
         case GEMM_M16:
-            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
+            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         case GEMM_M64:
-            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
+            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         case GEMM_M128:
-            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
+            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         default:
-            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, st);
+            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
     }
 }
 
@@ -722,8 +726,10 @@ hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
                                   const void* w_in, const void* w_up, const void* w_out,
                                   void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                   long long max_tiles, int H, int F, int swiglu,
-                                  hipStream_t st) {
+                                  const hipEvent_t* ev, hipStream_t st) {
     const dim3 blk(256);
+    hipError_t e;
+    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
     const dim3 g1((unsigned)max_tiles, (unsigned)((F + 63) / 64));
     const float* A = (const float*)a;
     if (swiglu) {
@@ -737,11 +743,14 @@ hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
         else
             hipLaunchKernelGGL((k_grouped_gemm_f32<1, 1, false>), g1, blk, 0, st, A, nullptr, (const float*)w_in, nullptr, (float*)h, tiles, ntiles, H, F);
     }
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const dim3 g2((unsigned)max_tiles, (unsigned)((H + 63) / 64));
     hipLaunchKernelGGL((k_grouped_gemm_f32<1, 0, false>), g2, blk, 0, st, (const float*)h, nullptr, (const float*)w_out, nullptr, (float*)y, tiles, ntiles, F, H);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+    return e;
 }
 
 }  // namespace moe

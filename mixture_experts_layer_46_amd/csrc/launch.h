@@ -43,17 +43,18 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, Tile* tiles
 
 // grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]]
 // with x holding a_rows rows (its bytes must stay below 2^32 for the 32-bit buffer
-// offsets of the row-tile kernels).
+// offsets of the row-tile kernels).  ev: NULL, or three events recorded on `st` before
+// the first projection, between the two projections and after the second.
 hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_t* gather_rows,
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   hipStream_t st);
+                                   const hipEvent_t* ev, hipStream_t st);
 hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
                                   const void* w_in, const void* w_up, const void* w_out,
                                   void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                   long long max_tiles, int H, int F, int swiglu,
-                                  hipStream_t st);
+                                  const hipEvent_t* ev, hipStream_t st);
 
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of_pair, const float* w,
                           void* out, long long T, int k, int H, int dtype, hipStream_t st);

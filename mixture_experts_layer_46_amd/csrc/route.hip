@@ -256,6 +256,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 // -------------------------------------------------------------------- launchers
 int gate_splits(long long T, int H, int E) {
+    if (T <= 0) return 1;
     const long long tm = T <= 256 ? 16 : 64;
     const long long base = ((T + tm - 1) / tm) * ((E + GT_E - 1) / GT_E);
     long long sp = (512 + base - 1) / base;

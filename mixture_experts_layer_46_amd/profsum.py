@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the MoE kernels (text, a few KB).
+
+    python -m mixture_experts_layer_46_amd.profsum stats  <kernel_stats.csv> <out.txt> --command CMD
+    python -m mixture_experts_layer_46_amd.profsum traffic <fetch_counter_collection.csv>
+        <write_counter_collection.csv> <out.txt> --workload NAME --command CMD
+
+`stats` tabulates calls and mean/min/max duration of each moe:: kernel from a
+`--kernel-trace --stats` run.  `traffic` averages FETCH_SIZE and WRITE_SIZE (KiB per
+dispatch) of each moe:: kernel and scales them to HBM bytes with the factor the same
+counters give for the largest device copy in the run (a 1 GiB copy that the benchmark
+makes with --copy-calibration: true bytes / counted bytes).  The traffic file also
+records the sha256 of the grouped-GEMM source it was measured on, so a reader can tell
+when the kernel has changed since.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(HERE, "csrc", "grouped_gemm.hip")
+COPY_BYTES = 1 << 30
+
+
+def short_name(name: str) -> str:
+    """Kernel name without the argument list ('void moe::k<..>(...)' -> 'k<..>')."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            n = n[:i]
+            break
+    return n.replace("moe::", "")
+
+
+def _is_moe(name: str) -> bool:
+    return "moe::" in name
+
+
+def stats(csv_path: str, out_path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# rocprofv3 kernel-trace summary (MoE kernels)", f"# command: {command}", "",
+             f"{'calls':>6} {'mean_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel"]
+    for r in rows:
+        if not _is_moe(r["Name"]):
+            continue
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f}  {short_name(r['Name'])}")
+    text = "\n".join(lines) + "\n"
+    open(out_path, "w").write(text)
+    return text
+
+
+def _per_kernel(csv_path: str, counter: str):
+    vals = collections.defaultdict(list)
+    copies = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if _is_moe(r["Kernel_Name"]):
+            vals[short_name(r["Kernel_Name"])].append(v)
+        elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
+            copies.append(v)
+    return vals, (max(copies) if copies else None)
+
+
+def traffic(fetch_csv: str, write_csv: str, out_path: str, workload: str, command: str,
+            up: str | None = None, down: str | None = None) -> str:
+    fetch, copy_f = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write, copy_w = _per_kernel(write_csv, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024
+    f_scale = kib / copy_f if copy_f and 0.5 * kib < copy_f < 2 * kib else None
+    w_scale = kib / copy_w if copy_w and 0.5 * kib < copy_w < 2 * kib else None
+    digest = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    lines = ["# rocprofv3 PMC traffic summary (MoE kernels): FETCH_SIZE and WRITE_SIZE, KiB per",
+             "# dispatch, averaged over dispatches, then scaled by the copy calibration",
+             f"# command: {command}",
+             f"workload: {workload}",
+             f"grouped_gemm.hip sha256: {digest}",
+             f"copy calibration fetch KiB counted for 1 GiB: {copy_f}",
+             f"copy calibration write KiB counted for 1 GiB: {copy_w}",
+             f"fetch scale: {f_scale}",
+             f"write scale: {w_scale}", ""]
+    lines.append(f"{'dispatches':>10} {'fetch_KiB':>14} {'write_KiB':>14} {'hbm_MB':>10}  kernel")
+    per = {}
+    for name in sorted(set(fetch) | set(write)):
+        fv = sum(fetch[name]) / len(fetch[name]) if fetch.get(name) else 0.0
+        wv = sum(write[name]) / len(write[name]) if write.get(name) else 0.0
+        hbm = None
+        if f_scale and w_scale:
+            hbm = (fv * f_scale + wv * w_scale) * 1024
+        per[name] = hbm
+        hs = f"{hbm / 1e6:10.1f}" if hbm is not None else f"{'n/a':>10}"
+        lines.append(f"{len(fetch.get(name, [])):10d} {fv:14.1f} {wv:14.1f} {hs}  {name}")
+    lines.append("")
+    for which, pat in (("up", up), ("down", down)):
+        if not pat:
+            continue
+        hit = [n for n in per if n.startswith(pat)]
+        if len(hit) == 1 and per[hit[0]] is not None:
+            lines.append(f"{which} kernel: {pat}")
+            lines.append(f"{which} hbm bytes per launch: {per[hit[0]]:.0f}")
+    text = "\n".join(lines) + "\n"
+    open(out_path, "w").write(text)
+    return text
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("out")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("out")
+    b.add_argument("--workload", required=True)
+    b.add_argument("--command", required=True)
+    b.add_argument("--up", default=None, help="name prefix of the first-projection kernel")
+    b.add_argument("--down", default=None, help="name prefix of the second-projection kernel")
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(stats(args.csv, args.out, args.command), end="")
+    else:
+        print(traffic(args.fetch_csv, args.write_csv, args.out, args.workload, args.command,
+                      args.up, args.down), end="")
+
+
+if __name__ == "__main__":
+    main()
