@@ -341,10 +341,15 @@ __device__ __attribute__((always_inline)) inline void kstep(
     if (do_dma) dma_step<BM, NMAT>(nxt, ra, rb0, rb1, pl, kt_dma, K, rowB, wave);
     const lds_char* As = cur;
     const lds_char* Bs = cur + S::A_STAGE;
+    // Every fragment read of the step is issued before its first MFMA (A row block 0,
+    // then the B columns, then the other A row blocks, in the order the MFMAs use them),
+    // so the MFMAs wait on the LDS counter step by step instead of paying the LDS
+    // latency once per A row block.
     bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    auto read_a = [&](int fm) {
         af[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(As + a_rd + fm * 16 * S::BK * 2);
+    };
+    read_a(0);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         int mat, blk;                          // W matrix and its 16-column block
@@ -361,6 +366,9 @@ __device__ __attribute__((always_inline)) inline void kstep(
         const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         bfr[fn] = __builtin_bit_cast(bf16x8_t, v);
     }
+#pragma unroll
+    for (int fm = 1; fm < FM; ++fm) read_a(fm);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll

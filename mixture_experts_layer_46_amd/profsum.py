@@ -48,7 +48,8 @@ def _is_moe(name: str) -> bool:
 
 def stats(csv_path: str, out_path: str, command: str) -> str:
     rows = list(csv.DictReader(open(csv_path)))
-    lines = ["# rocprofv3 kernel-trace summary (MoE kernels)", f"# command: {command}", "",
+    lines = ["# rocprofv3 kernel-trace summary (MoE kernels)", f"# command: {command}",
+             f"# summary: python3 -m mixture_experts_layer_46_amd.profsum stats {csv_path} {out_path}", "",
              f"{'calls':>6} {'mean_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}  kernel"]
     for r in rows:
         if not _is_moe(r["Name"]):
@@ -86,6 +87,7 @@ def traffic(fetch_csv: str, write_csv: str, out_path: str, workload: str, comman
     lines = ["# rocprofv3 PMC traffic summary (MoE kernels): FETCH_SIZE and WRITE_SIZE, KiB per",
              "# dispatch, averaged over dispatches, then scaled by the copy calibration",
              f"# command: {command}",
+             f"# summary: python3 -m mixture_experts_layer_46_amd.profsum traffic {fetch_csv} {write_csv} {out_path}",
              f"workload: {workload}",
              f"grouped_gemm.hip sha256: {digest}",
              f"copy calibration fetch KiB counted for 1 GiB: {copy_f}",
