@@ -39,7 +39,9 @@
  *   - No C++ exception crosses this interface.
  *
  * Limits of this version: 1 <= E <= 256; 1 <= k <= min(E, 8); H % 8 == 0; F % 8 == 0;
- * T * k < 2^31; T*H and T*k*max(H,F) < 2^62 elements.
+ * T * k < 2^31; T*H and T*k*max(H,F) < 2^62 elements; x (T*H elements) and one expert
+ * matrix with 128 extra rows ((H+128)*F and (F+128)*H elements) below 4 GiB each, since
+ * the grouped GEMM addresses them with 32-bit byte offsets (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -90,6 +90,13 @@ moe_status check_shape(const moe_shape* s) {
     if (s->T >= (1ll << 31) || P >= (1ll << 31)) return fail(MOE_ERR_SHAPE, "T*k = %lld >= 2^31", P);
     const long long mx = s->H > s->F ? s->H : s->F;
     if ((double)P * (double)mx >= 4.0e18) return fail(MOE_ERR_SHAPE, "T*k*max(H,F) too large");
+    // the grouped GEMM addresses one expert matrix (plus up to 128 rows past its end) and
+    // the token matrix x with 32-bit byte offsets
+    const long long es = s->dtype == MOE_F32 ? 4 : 2;
+    if (((long long)s->H + 128) * s->F * es >= (1ll << 32) || ((long long)s->F + 128) * s->H * es >= (1ll << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "one expert matrix (H=%d x F=%d) must stay below 4 GiB", s->H, s->F);
+    if (s->T * (long long)s->H * es >= (1ll << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "x (T=%lld x H=%d) must stay below 4 GiB", (long long)s->T, s->H);
     return MOE_OK;
 }
 

@@ -319,26 +319,31 @@ __device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t r
 #pragma unroll
     for (int i = 0; i < BDMA; ++i) {
         const int j = wave * BDMA + i;
+        // rows k0 >= K fall past the resource's K * rowB bytes and read zeros (the host
+        // keeps (K + 128) * rowB below 2^32, so the offset cannot wrap)
         const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && j >= 8) ? rb1 : rb0,
                                                  (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
     }
 }
 
-// One K step: start the DMA of step kt_dma into `nxt` (if do_dma), then read this
-// step's fragments from `cur` and run its MFMAs.  `cur` and `nxt` are distinct stages;
-// saying so with __restrict__ lets the compiler issue the reads without waiting for
-// the DMA just started.
+// One K step: read this step's fragments from `cur`, start the DMA of step kt_dma into
+// `nxt`, and run the step's MFMAs with the DMA instructions spread between them (a
+// burst of DMA issues at the start of the step can stall the wavefront while the
+// texture-address queue drains).  Steps past the end of K load from an out-of-range
+// offset, which reads zeros into a stage nobody reads, so every step issues the same
+// number of DMA instructions and the wait count stays constant.  `cur` and `nxt` are
+// distinct stages; saying so with __restrict__ lets the compiler issue the reads
+// without waiting for DMA in flight.
 template <int BM, int NMAT>
 __device__ __attribute__((always_inline)) inline void kstep(
-    const lds_char* __restrict__ cur, lds_char* __restrict__ nxt, bool do_dma, __amdgpu_buffer_rsrc_t ra,
+    const lds_char* __restrict__ cur, lds_char* __restrict__ nxt, __amdgpu_buffer_rsrc_t ra,
     __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int kt_dma, int K, uint32_t rowB,
     int wave, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
     using S = LdsShape<BM, NMAT>;
     constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
-    if (do_dma) dma_step<BM, NMAT>(nxt, ra, rb0, rb1, pl, kt_dma, K, rowB, wave);
     const lds_char* As = cur;
     const lds_char* Bs = cur + S::A_STAGE;
     // Every fragment read of the step is issued before its first MFMA (A row block 0,
@@ -369,12 +374,28 @@ __device__ __attribute__((always_inline)) inline void kstep(
 #pragma unroll
     for (int fm = 1; fm < FM; ++fm) read_a(fm);
     __builtin_amdgcn_sched_barrier(0);
+    dma_step<BM, NMAT>(nxt, ra, rb0, rb1, pl, kt_dma, K, rowB, wave);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+    // issue order: one DMA instruction, then FM*FN/DPW MFMAs, DPW times
+    constexpr int PER = FM * FN / S::DPW > 0 ? FM * FN / S::DPW : 1;
+#pragma unroll
+    for (int i = 0; i < S::DPW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (the LDS DMA)
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // MFMA
+    }
 }
+
+// Workgroup barrier of the K loop.  Each wavefront has already waited for its own DMA
+// of the step (wait_dma) and its fragment reads of the previous step were consumed by
+// MFMAs before it arrives, so the barrier alone makes the stage complete for all and the
+// stage being refilled free.  It is written without __syncthreads' memory fence, which
+// otherwise leads the compiler to drain every DMA in flight (vmcnt(0)) at each step; the
+// memory clobber still keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Wait until at most `pending` K steps' DMA of this wavefront are still in flight.
 template <int DPW>
@@ -471,26 +492,26 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // prologue: steps 0..NSTAGE-2 in flight
-        for (int t = 0; t < NSTAGE - 1 && t < KT; ++t)
+        // prologue: steps 0..NSTAGE-2 in flight (steps past K read zeros, see kstep)
+#pragma unroll
+        for (int t = 0; t < NSTAGE - 1; ++t)
             dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
         if (wave_rows) {
             for (int kt = 0; kt < KT; ++kt) {
-                wait_dma<S::DPW>(min(kt + NSTAGE - 2, KT - 1) - kt);
-                __syncthreads();
+                wait_dma<S::DPW>(NSTAGE - 2);
+                kloop_barrier();
                 kstep<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
-                                kt + NSTAGE - 1 < KT, ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd,
-                                b_rd, g, wn, acc);
+                                ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
             }
         } else {       // no rows for this wavefront: it still moves its share of the tiles
             for (int kt = 0; kt < KT; ++kt) {
-                wait_dma<S::DPW>(min(kt + NSTAGE - 2, KT - 1) - kt);
-                __syncthreads();
-                if (kt + NSTAGE - 1 < KT)
-                    dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
-                                       kt + NSTAGE - 1, K, rowB, wave);
+                wait_dma<S::DPW>(NSTAGE - 2);
+                kloop_barrier();
+                dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
+                                   kt + NSTAGE - 1, K, rowB, wave);
             }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
         __syncthreads();
 
         constexpr int FO = (NMAT == 2) ? FN / 2 : FN;

@@ -61,6 +61,8 @@ def _ws(lib, s):
     (dict(k=9, E=8), 2), (dict(E=257, k=2), 3), (dict(E=64, k=9), 3), (dict(H=60), 3),
     (dict(F=100), 3), (dict(dtype=7), 3), (dict(ffn=5), 3), (dict(flags=0x10), 3),
     (dict(capacity=-1), 2), (dict(T=1 << 31, k=1), 2), (dict(T=1 << 30, k=2), 2),
+    # 32-bit byte offsets of the grouped GEMM: an expert matrix or x of 4 GiB or more
+    (dict(H=65536, F=32768), 3), (dict(H=8, F=1 << 24), 3), (dict(T=300000, H=8192), 3),
 ])
 def test_bad_shapes_are_rejected(lib, kw, code):
     s = _shape(**kw)
