@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 // straight into LDS with buffer_load_dwordx4 ... lds (lane i's 16 bytes land in slot i
 // of the wavefront's 1 KB); a buffer resource bounds each operand, so chunks past K,
 // N or the tile's rows read as zeros and no register stages the tiles.
-//   * A (rows, k-contiguous): LDS [BM][32], chunk q of row m at q ^ ((m >> 2) & 3);
+//   * A (rows, k-contiguous): LDS [BM][32], chunk q of row m at q ^ ((m >> 1) & 2);
 //     fragments are ds_read_b128.
 //   * W (k rows, n-contiguous), kept as in memory: LDS [32][256] (SiLU2 and the second
 //     projection) or [2][32][128] (SwiGLU gate | up), 16-byte chunk c of row k at
@@ -273,7 +273,12 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int fk(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
-__device__ __forceinline__ int swa4(int m) { return (m >> 2) & 3; }
+// A-row swizzle: 16-byte chunk q of tile row m sits at slot q ^ swa4(m).  On gfx950 a
+// ds_read_b128 serves 16 lanes per LDS cycle (64 banks), grouped by bit2^bit3^bit4 of
+// the lane index (lanes 0-3, 12-15 and 20-27 share a cycle; measured with the bank-
+// conflict counter); a fragment read has lane l on row l & 15, chunk l >> 4.  With
+// swa4(m) = (m >> 1) & 2 the 16 lanes of every cycle land on distinct bank quads.
+__device__ __forceinline__ int swa4(int m) { return (m >> 1) & 2; }
 
 constexpr uint32_t kOOB = 0x80000000u;          // an offset past every buffer: reads zeros
 
