@@ -163,7 +163,7 @@ def _gemm_kernel_name(cfg, up: bool) -> str:
         return "k_grouped_gemm_f32<%d, %d, %s>" % ((2 if cfg.ffn == "swiglu" else 1) if up else 1,
                                                     1 if up else 0, "true" if up else "false")
     mean = cfg.T * cfg.k / cfg.E
-    bm = 16 if mean <= 24 else 64 if mean <= 80 else 128 if mean <= 160 else 256
+    bm = 16 if mean <= 24 else 64 if mean <= 80 else 128 if mean <= 160 else 320 if mean <= 288 else 256
     nmat = (2 if cfg.ffn == "swiglu" else 1) if up else 1
     if bm == 16:
         return "k_grouped_gemm_bf16<16, 256, %d, 1, %d, %s>" % (nmat, 1 if up else 0,

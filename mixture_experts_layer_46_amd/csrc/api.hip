@@ -1,5 +1,6 @@
 // C ABI of the MoE layer forward: argument checks, workspace carve-up, launches.
 // Declarations, argument meaning, layouts, ownership and error behaviour: include/moe.h.
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -130,7 +131,7 @@ GemmCfg pick_cfg(const moe_shape& s) {
     if (mean <= 24) return GEMM_M16;
     if (mean <= 80) return GEMM_M64;
     if (mean <= 160) return GEMM_M128;
-    return GEMM_M256;
+    return GEMM_M256;                    // 256 or 320 rows, chosen on the device
 }
 
 moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_rows,
@@ -144,17 +145,18 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     int32_t* ntiles = at<int32_t>(ws, L.ntiles);
     if (s.dtype == MOE_F32) {
         const int BM = 64;
-        HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
+        HIPCHK(launch_build_tiles(offsets, s.E, BM, BM, 1, 1, tiles, ntiles, st), "build_tiles");
         HIPCHK(launch_grouped_ffn_f32(a, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
                                       ntiles, max_tiles_for(P, s.E, BM), s.H, s.F, swiglu, ev, st),
                "grouped_ffn_f32");
         return MOE_OK;
     }
     const GemmCfg cfg = pick_cfg(s);
-    const int BM = gemm_cfg_bm(cfg);
-    HIPCHK(launch_build_tiles(offsets, s.E, BM, tiles, ntiles, st), "build_tiles");
+    int bma, bmb;
+    gemm_cfg_heights(cfg, &bma, &bmb);
+    HIPCHK(launch_build_tiles_for(offsets, s.E, cfg, s.H, s.F, swiglu, tiles, ntiles, st), "build_tiles");
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
-                                   ntiles, max_tiles_for(P, s.E, BM), cfg, s.H, s.F, swiglu, ev, st),
+                                   ntiles, max_tiles_for(P, s.E, std::min(bma, bmb)), cfg, s.H, s.F, swiglu, ev, st),
            "grouped_ffn_bf16");
     return MOE_OK;
 }

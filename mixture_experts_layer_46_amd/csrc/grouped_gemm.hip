@@ -33,6 +33,8 @@
 //     and column blocks that share a row tile, meet in the same L2.
 //   * The epilogue applies SiLU / SwiGLU in fp32, rounds to bf16 once, stages the tile
 //     in LDS and writes whole rows with 16-byte stores.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -253,7 +255,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 //   * A (rows, k-contiguous): LDS [BM][32], chunk q of row m at q ^ ((m >> 1) & 2);
 //     fragments are ds_read_b128.
 //   * W (k rows, n-contiguous), kept as in memory: LDS [32][256] (SiLU2 and the second
-//     projection) or [2][32][128] (SwiGLU gate | up), 16-byte chunk c of row k at
+//     projection) or [2][32][128] (SwiGLU gate | up; 192 and 2 x 96 of them used by the
+//     320-row tile), 16-byte chunk c of row k at
 //     c ^ fk(k), fk(k) = 2 * ((k & 3) | ((k >> 3) & 1) << 2).  The MFMA operand (8
 //     consecutive k of one column per lane) comes from two ds_read_b64_tr_b16 (gfx950):
 //     within each group of 16 lanes, source lane j reads 4 consecutive columns of row
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 //     (s_waitcnt vmcnt(<DMA issued after this stage>)).
 //   * 256 x 256 tile, 4 wavefronts of 128 x 128 (v_mfma_f32_16x16x32_bf16, fp32
 //     accumulators in AGPRs), which halves the bytes moved per FLOP against 128-row
-//     tiles; 128- and 64-row tiles use the same code with shorter wavefront tiles.
+//     tiles; 128- and 64-row tiles use the same code with shorter wavefront tiles, and
+//     the 320 x 192 tile with wavefront tiles of 160 x 96.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -286,15 +290,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Tile shapes: BM x BN outputs (BN over both matrices for SwiGLU).  The 320-row tile is
+// 192 wide so that its accumulators (60 16x16 blocks per wavefront) still fit the AGPRs;
+// it lets one tile hold every row of an expert with up to 320 rows, so the expert's
+// weight slice is streamed once.  The LDS weight rows stay LBN = 256 columns wide in
+// every shape (only BN are filled and read), which keeps one swizzle for all of them.
 template <int BM, int NMAT>
 struct LdsShape {
-    static constexpr int BN = 256, BNm = BN / NMAT, WAVES_M = 2, WAVES_N = 2, BK = 32, NSTAGE = 4;
+    static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, WAVES_M = 2, WAVES_N = 2, BK = 32;
+    static constexpr int NSTAGE = 4, LBN = 256, LBNm = LBN / NMAT;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
-    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * BN * 2, STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2, STAGE = A_STAGE + B_STAGE;
     static constexpr int ADMA = A_STAGE / 1024 / 4;   // A DMA instructions per wavefront per step
     static constexpr int BDMA = B_STAGE / 1024 / 4;   // W DMA instructions per wavefront per step
     static constexpr int DPW = ADMA + BDMA;
-    static constexpr int BROW = 2 * BNm;              // LDS bytes per W row
+    static constexpr int BROW = 2 * LBNm;             // LDS bytes per W row
     static constexpr int CS_STRIDE = BNm + 8;
     static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
                                             ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
@@ -410,9 +420,10 @@ __device__ __forceinline__ void wait_dma(int pending) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// All work items of one launch for row tiles of height BM (the persistent loop).
 template <int BM, int NMAT, int ACT, bool GATHER>
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
+__device__ __forceinline__ void gemm_tiles(
+    uint4* smem, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
     long long a_rows) {
@@ -423,7 +434,6 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     static_assert(ADMA >= 1 && BDMA >= 1, "every wavefront moves part of each operand");
     static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
 
-    extern __shared__ uint4 smem[];
     lds_char* lds = (lds_char*)smem;
     bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
 
@@ -488,7 +498,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
                 c = (lane & 15) ^ fk(k);
             }
             const uint32_t col = (uint32_t)(n0 + 8 * c);
-            pl.b_off[i] = col < (uint32_t)N ? (uint32_t)k * rowB + col * 2 : kOOB;
+            // chunks past the tile's BNm columns (320-row tile) or past N are not loaded
+            pl.b_off[i] = (8 * c < BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
         }
 
         f32x4_t acc[FM][FN];
@@ -550,19 +561,66 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     }
 }
 
+// The grouped GEMM kernel.  BMA and BMB are the row-tile heights the tile list may use
+// (equal for the 64- and 128-row kernels); the tile builder chose one from the actual
+// per-expert counts and stored it in ntiles_p[1], so one launch runs one shape.
+template <int BMA, int BMB>
+struct LdsPair {
+    template <int NMAT>
+    static constexpr size_t bytes() {
+        return LdsShape<BMA, NMAT>::LDS_BYTES > LdsShape<BMB, NMAT>::LDS_BYTES ? LdsShape<BMA, NMAT>::LDS_BYTES
+                                                                               : LdsShape<BMB, NMAT>::LDS_BYTES;
+    }
+};
+
+template <int BMA, int BMB, int NMAT, int ACT, bool GATHER>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
+    long long a_rows) {
+    extern __shared__ uint4 smem[];
+    if (BMA != BMB && __builtin_amdgcn_readfirstlane(ntiles_p[1]) == BMB)
+        gemm_tiles<BMB, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+    else
+        gemm_tiles<BMA, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+}
+
 // ------------------------------------------------------------------------ tile list
-// One workgroup of 256 threads (E <= 256): expert e gets ceil(count_e / BM) tiles.
+// One workgroup of 256 threads (E <= 256).  Two candidate row-tile heights BMA and BMB
+// (equal when the kernel has one shape): with wa / wb column blocks per row tile (both
+// projections), the height giving fewer work items, sum_e ceil(count_e / BM) * w, wins
+// (BMA on a tie).  Every item costs about the same K steps whatever its rows, so the
+// item count is the cost.  Expert e then gets ceil(count_e / BM) tiles; ntiles[0] is the
+// tile count and ntiles[1] the height chosen.
 __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__ offsets, int E,
-                                                     int BM, Tile* __restrict__ tiles,
+                                                     int BMA, int BMB, int wa, int wb,
+                                                     Tile* __restrict__ tiles,
                                                      int32_t* __restrict__ ntiles) {
     __shared__ int buf[2][256];
-    const int e = threadIdx.x;
-    int r0 = 0, r1 = 0, nt = 0;
+    __shared__ long long cost[2][4];
+    const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+    int r0 = 0, r1 = 0;
     if (e < E) {
         r0 = offsets[e];
         r1 = offsets[e + 1];
-        nt = (r1 - r0 + BM - 1) / BM;
     }
+    long long ca = (long long)((r1 - r0 + BMA - 1) / BMA) * wa;
+    long long cb = (long long)((r1 - r0 + BMB - 1) / BMB) * wb;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        ca += __shfl_xor(ca, off);
+        cb += __shfl_xor(cb, off);
+    }
+    if (lane == 0) {
+        cost[0][wave] = ca;
+        cost[1][wave] = cb;
+    }
+    __syncthreads();
+    const long long ta = cost[0][0] + cost[0][1] + cost[0][2] + cost[0][3];
+    const long long tb = cost[1][0] + cost[1][1] + cost[1][2] + cost[1][3];
+    const int BM = tb < ta ? BMB : BMA;
+    const int nt = (r1 - r0 + BM - 1) / BM;
     int cur = 0;
     buf[0][e] = nt;
     __syncthreads();
@@ -575,22 +633,49 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
     const int incl = buf[cur][e];
     const int base = incl - nt;
     for (int i = 0; i < nt; ++i) tiles[base + i] = Tile{e, r0 + i * BM, min(r0 + (i + 1) * BM, r1), base, nt, 0, 0, 0};
-    if (e == 255) *ntiles = incl;
+    if (e == 255) {
+        ntiles[0] = incl;
+        ntiles[1] = BM;
+    }
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, Tile* tiles,
-                              int32_t* ntiles, hipStream_t st) {
-    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(256), 0, st, offsets, E, BM, tiles, ntiles);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int BMA, int BMB, int wa, int wb,
+                              Tile* tiles, int32_t* ntiles, hipStream_t st) {
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(256), 0, st, offsets, E, BMA, BMB, wa, wb, tiles, ntiles);
     return hipGetLastError();
 }
 
-int gemm_cfg_bm(GemmCfg c) {
+void gemm_cfg_heights(GemmCfg c, int* bma, int* bmb) {
     switch (c) {
-        case GEMM_M16: return 16;
-        case GEMM_M64: return 64;
-        case GEMM_M128: return 128;
-        default: return 256;
+        case GEMM_M16: *bma = *bmb = 16; return;
+        case GEMM_M64: *bma = *bmb = 64; return;
+        case GEMM_M128: *bma = *bmb = 128; return;
+        default: *bma = 256; *bmb = 320; return;     // chosen per launch by the tile builder
     }
+}
+
+// Column blocks of one row tile over both projections (first: N = F, second: N = H).
+static int col_blocks(int BM, int H, int F, int swiglu) {
+    int bn1, bn2;
+    if (BM < 64) {
+        bn1 = swiglu ? 128 : 256;
+        bn2 = 256;
+    } else if (BM == 320) {
+        bn1 = swiglu ? LdsShape<320, 2>::BNm : LdsShape<320, 1>::BNm;
+        bn2 = LdsShape<320, 1>::BNm;
+    } else {
+        bn1 = swiglu ? LdsShape<256, 2>::BNm : LdsShape<256, 1>::BNm;
+        bn2 = LdsShape<256, 1>::BNm;
+    }
+    return (F + bn1 - 1) / bn1 + (H + bn2 - 1) / bn2;
+}
+
+hipError_t launch_build_tiles_for(const int32_t* offsets, int E, GemmCfg cfg, int H, int F, int swiglu,
+                                  Tile* tiles, int32_t* ntiles, hipStream_t st) {
+    int a, b;
+    gemm_cfg_heights(cfg, &a, &b);
+    return launch_build_tiles(offsets, E, a, b, col_blocks(a, H, F, swiglu), col_blocks(b, H, F, swiglu),
+                              tiles, ntiles, st);
 }
 
 // ------------------------------------------------------------------------ launching
@@ -618,7 +703,7 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
     return hipSuccess;
 }
 
-template <int BM, int NMAT, int WAVES_M, int ACT, bool GATHER>
+template <int BM, int BMB, int NMAT, int WAVES_M, int ACT, bool GATHER>
 static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
                            const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
                            long long max_items, int K, int N, hipStream_t st) {
@@ -633,35 +718,36 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
                            (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N);
     } else {
-        using S = LdsShape<BM, NMAT>;
-        auto kern = k_grouped_gemm_lds<BM, NMAT, ACT, GATHER>;
-        hipError_t e = persistent_grid(kern, S::LDS_BYTES, ready, occ, max_items, G);
+        constexpr size_t lds_bytes = LdsPair<BM, BMB>::template bytes<NMAT>();
+        auto kern = k_grouped_gemm_lds<BM, BMB, NMAT, ACT, GATHER>;
+        hipError_t e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
+        hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
                            (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
     }
     return hipGetLastError();
 }
 
-template <int BM, int WAVES_M>
+template <int BM, int BMB, int WAVES_M>
 static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather_rows, const void* w_in,
                           const void* w_up, const void* w_out, void* h, void* y,
                           const Tile* tiles, const int32_t* ntiles, long long max_tiles,
                           int H, int F, int swiglu, const hipEvent_t* ev, hipStream_t st) {
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-    const long long items1 = max_tiles * ((F + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256));
+    // work items (row tiles x column blocks) bound the persistent grid: the larger of the
+    // two shapes' counts (max_tiles is counted for the lower height)
+    const long long items = max_tiles * std::max(col_blocks(BM, H, F, swiglu), col_blocks(BMB, H, F, swiglu));
     if (swiglu) {
-        e = gather_rows ? run_gemm<BM, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items1, H, F, st)
-                        : run_gemm<BM, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items1, H, F, st);
+        e = gather_rows ? run_gemm<BM, BMB, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items, H, F, st)
+                        : run_gemm<BM, BMB, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items, H, F, st);
     } else {
-        e = gather_rows ? run_gemm<BM, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items1, H, F, st)
-                        : run_gemm<BM, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items1, H, F, st);
+        e = gather_rows ? run_gemm<BM, BMB, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items, H, F, st)
+                        : run_gemm<BM, BMB, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items, H, F, st);
     }
     if (e != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-    const long long items2 = max_tiles * ((H + 255) / 256);
-    e = run_gemm<BM, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items2, F, H, st);
+    e = run_gemm<BM, BMB, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items, F, H, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     return e;
 }
@@ -673,13 +759,13 @@ hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_
                                    const hipEvent_t* ev, hipStream_t st) {
     switch (cfg) {
         case GEMM_M16:
-            return run_ffn<16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<16, 16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         case GEMM_M64:
-            return run_ffn<64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<64, 64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         case GEMM_M128:
-            return run_ffn<128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<128, 128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
         default:
-            return run_ffn<256, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<256, 320, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
     }
 }
 

@@ -19,9 +19,11 @@ struct Tile {
     int e, row0, row1, first, cnt, pad0, pad1, pad2;
 };
 
-// Tile configurations of the bf16 grouped GEMM.
+// Tile configurations of the bf16 grouped GEMM.  GEMM_M256 lets the tile builder choose
+// 256- or 320-row tiles per launch from the actual per-expert counts.
 enum GemmCfg { GEMM_M16 = 0, GEMM_M64 = 1, GEMM_M128 = 2, GEMM_M256 = 3 };
-int gemm_cfg_bm(GemmCfg c);
+// the row-tile heights a configuration may use (*bma == *bmb: one shape)
+void gemm_cfg_heights(GemmCfg c, int* bma, int* bmb);
 
 // K splits of the gate projection (partial sums [splits][T][E]) for a layer shape
 int gate_splits(long long T, int H, int E);
@@ -38,8 +40,13 @@ hipError_t launch_group(const int32_t* topk_idx, long long P, int k, int E, int 
 hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                          int E, void* x_perm, long long P, int H, int esize, hipStream_t st);
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int BM, Tile* tiles,
-                              int32_t* ntiles, hipStream_t st);
+// tile list for heights BMA / BMB (the one with fewer work items; wa, wb = column blocks
+// per row tile); ntiles[0] = tile count, ntiles[1] = the height chosen
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int BMA, int BMB, int wa, int wb,
+                              Tile* tiles, int32_t* ntiles, hipStream_t st);
+// the same for a bf16 configuration of the grouped FFN
+hipError_t launch_build_tiles_for(const int32_t* offsets, int E, GemmCfg cfg, int H, int F, int swiglu,
+                                  Tile* tiles, int32_t* ntiles, hipStream_t st);
 
 // grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]]
 // with x holding a_rows rows (its bytes must stay below 2^32 for the 32-bit buffer

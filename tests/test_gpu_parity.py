@@ -126,6 +126,9 @@ FFN_CASES = [  # T, H, E, k, F, ffn, dtype  (mean rows per expert picks the row 
     (24, 256, 16, 2, 512, "swiglu", "bf16"), (200, 200, 8, 2, 320, "silu2", "bf16"),
     (512, 264, 4, 2, 136, "swiglu", "bf16"), (100, 128, 1, 1, 128, "silu2", "bf16"),
     (300, 128, 256, 8, 64, "swiglu", "bf16"), (700, 192, 4, 2, 2056, "swiglu", "bf16"),
+    # ~275 rows per expert: the tile builder picks 320 x 192 tiles (8 items against ~16 x
+    # the column blocks of 256-row tiles); ragged K and N against 192 (96 per SwiGLU matrix)
+    (1100, 520, 8, 2, 392, "silu2", "bf16"), (1100, 264, 8, 2, 200, "swiglu", "bf16"),
 ]
 
 
@@ -180,6 +183,8 @@ E2E = [
     MoEConfig("one_expert", T=100, H=128, E=1, k=1, F=128, ffn="silu2", dtype="bf16", bias="none"),
     MoEConfig("skew_256", T=300, H=128, E=256, k=8, F=64, ffn="swiglu", dtype="bf16", bias="zipf1.1"),
     MoEConfig("one_token", T=1, H=64, E=8, k=2, F=64, ffn="swiglu", dtype="bf16", bias="none"),
+    # 320-row tiles with skewed counts: hot experts span several tiles, cold ones a few rows
+    MoEConfig("tiles_320_skew", T=1200, H=520, E=16, k=3, F=392, ffn="silu2", dtype="bf16", bias="zipf1.1"),
 ]
 
 
