@@ -349,8 +349,10 @@ __device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t r
 // offset, which reads zeros into a stage nobody reads, so every step issues the same
 // number of DMA instructions and the wait count stays constant.  `cur` and `nxt` are
 // distinct stages; saying so with __restrict__ lets the compiler issue the reads
-// without waiting for DMA in flight.
-template <int BM, int NMAT>
+// without waiting for DMA in flight.  Only the first FMA 16-row blocks of the wavefront
+// tile hold rows of the tile (FMA < FM for short experts), so only they are read and
+// multiplied.
+template <int BM, int NMAT, int FMA>
 __device__ __attribute__((always_inline)) inline void kstep(
     const lds_char* __restrict__ cur, lds_char* __restrict__ nxt, __amdgpu_buffer_rsrc_t ra,
     __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
@@ -358,7 +360,7 @@ __device__ __attribute__((always_inline)) inline void kstep(
     int wave, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
     using S = LdsShape<BM, NMAT>;
-    constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
+    constexpr int FM = FMA, FN = S::FN, BROW = S::BROW;
     const lds_char* As = cur;
     const lds_char* Bs = cur + S::A_STAGE;
     // Every fragment read of the step is issued before its first MFMA (A row block 0,
@@ -401,6 +403,26 @@ __device__ __attribute__((always_inline)) inline void kstep(
     for (int i = 0; i < S::DPW; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (the LDS DMA)
         __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // MFMA
+    }
+}
+
+template <int DPW>
+__device__ __forceinline__ void wait_dma(int pending);
+__device__ __forceinline__ void kloop_barrier();
+
+// The K loop of one work item for a wavefront whose rows fill FMA 16-row blocks.
+template <int BM, int NMAT, int FMA>
+__device__ __attribute__((always_inline)) inline void kloop(
+    lds_char* lds, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K, uint32_t rowB, int wave,
+    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE;
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_dma<S::DPW>(NSTAGE - 2);
+        kloop_barrier();
+        kstep<BM, NMAT, FMA>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
+                             ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
     }
 }
 
@@ -513,12 +535,17 @@ __device__ __forceinline__ void gemm_tiles(
         for (int t = 0; t < NSTAGE - 1; ++t)
             dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
         if (wave_rows) {
-            for (int kt = 0; kt < KT; ++kt) {
-                wait_dma<S::DPW>(NSTAGE - 2);
-                kloop_barrier();
-                kstep<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
-                                ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
-            }
+            // a short expert fills only the first blocks of the wavefront tile: multiply
+            // just those (1, 2 or 4 blocks of 16 rows, else all)
+            const int wrows = rows - wm * WTM;
+            if (wrows <= 16)
+                kloop<BM, NMAT, 1>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+            else if (FM > 2 && wrows <= 32)
+                kloop<BM, NMAT, (FM > 2 ? 2 : FM)>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+            else if (FM > 4 && wrows <= 64)
+                kloop<BM, NMAT, (FM > 4 ? 4 : FM)>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+            else
+                kloop<BM, NMAT, FM>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
         } else {       // no rows for this wavefront: it still moves its share of the tiles
             for (int kt = 0; kt < KT; ++kt) {
                 wait_dma<S::DPW>(NSTAGE - 2);
