@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="pages_worked_shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
@@ -163,12 +163,14 @@ def _gemm_kernel_name(cfg, up: bool) -> str:
         return "k_grouped_gemm_f32<%d, %d, %s>" % ((2 if cfg.ffn == "swiglu" else 1) if up else 1,
                                                     1 if up else 0, "true" if up else "false")
     mean = cfg.T * cfg.k / cfg.E
-    bm = 16 if mean <= 24 else 64 if mean <= 80 else 128 if mean <= 160 else 320 if mean <= 288 else 256
     nmat = (2 if cfg.ffn == "swiglu" else 1) if up else 1
-    if bm == 16:
-        return "k_grouped_gemm_bf16<16, 256, %d, 1, %d, %s>" % (nmat, 1 if up else 0,
-                                                               "true" if up else "false")
-    return "k_grouped_gemm_lds<%d, %d, %d, %s>" % (bm, nmat, 1 if up else 0, "true" if up else "false")
+    act, gather = (1, "true") if up else (0, "false")
+    if mean <= 24:
+        return "k_grouped_gemm_bf16<16, 256, %d, 1, %d, %s>" % (nmat, act, gather)
+    # 64- and 128-row kernels have one tile height; above that the kernel holds 256- and
+    # 320-row tiles and the tile builder picks one per launch
+    pair = (64, 64) if mean <= 80 else (128, 128) if mean <= 160 else (256, 320)
+    return "k_grouped_gemm_lds<%d, %d, %d, %d, %s>" % (pair + (nmat, act, gather))
 
 
 def _roofline(kd, peak_flops):
