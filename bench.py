@@ -114,9 +114,9 @@ def main():
     flops = A.ffn_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn)
     peak_flops = A.PEAK_BF16_FLOPS if cfg.dtype == "bf16" else A.PEAK_FP32_FLOPS
     kernels = {
-        "up": dict(name=_gemm_kernel_name(cfg, up=True), ms=up_ms,
+        "up": dict(name=_gemm_kernel_name(cfg, True, counts), ms=up_ms,
                    flops=A.ffn_up_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn), bytes=sb.ffn_up),
-        "down": dict(name=_gemm_kernel_name(cfg, up=False), ms=down_ms,
+        "down": dict(name=_gemm_kernel_name(cfg, False, counts), ms=down_ms,
                      flops=A.ffn_down_flops(cfg.T, cfg.k, cfg.H, cfg.F), bytes=sb.ffn_down),
     }
     for kd in kernels.values():
@@ -156,9 +156,26 @@ def main():
     return 0
 
 
-def _gemm_kernel_name(cfg, up: bool) -> str:
-    """Name of the grouped-GEMM kernel a projection launches (as rocprofv3 lists it); the
-    tile height follows the library's choice from the mean rows per expert."""
+def _tile_height(cfg, counts) -> int:
+    """The row-tile height the library's tile builder picks for these per-expert counts
+    (256 or 320 rows: the one needing fewer work items, 256 on a tie)."""
+    import math
+    swiglu = cfg.ffn == "swiglu"
+
+    def blocks(bn1, bn2):
+        return math.ceil(cfg.F / bn1) + math.ceil(cfg.H / bn2)
+    wa = blocks(128 if swiglu else 256, 256)
+    wb = blocks(96 if swiglu else 192, 192)
+    ta = sum(math.ceil(int(c) / 256) for c in counts) * wa
+    tb = sum(math.ceil(int(c) / 320) for c in counts) * wb
+    return 320 if tb < ta else 256
+
+
+def _gemm_kernel_name(cfg, up: bool, counts) -> str:
+    """Name of the grouped-GEMM kernel a projection runs (as rocprofv3 lists it): the
+    kernel follows the mean rows per expert, and above 160 rows the tile height the
+    tile builder picks (256-row tiles run in the ping-pong kernel, 320-row ones in the
+    four-wavefront kernel)."""
     if cfg.dtype != "bf16":
         return "k_grouped_gemm_f32<%d, %d, %s>" % ((2 if cfg.ffn == "swiglu" else 1) if up else 1,
                                                     1 if up else 0, "true" if up else "false")
@@ -167,10 +184,13 @@ def _gemm_kernel_name(cfg, up: bool) -> str:
     act, gather = (1, "true") if up else (0, "false")
     if mean <= 24:
         return "k_grouped_gemm_bf16<16, 256, %d, 1, %d, %s>" % (nmat, act, gather)
-    # 64- and 128-row kernels have one tile height; above that the kernel holds 256- and
-    # 320-row tiles and the tile builder picks one per launch
-    pair = (64, 64) if mean <= 80 else (128, 128) if mean <= 160 else (256, 320)
-    return "k_grouped_gemm_lds<%d, %d, %d, %d, %s>" % (pair + (nmat, act, gather))
+    if mean <= 80:
+        return "k_grouped_gemm_lds<64, 64, %d, %d, %s>" % (nmat, act, gather)
+    if mean <= 160:
+        return "k_grouped_gemm_lds<128, 128, %d, %d, %s>" % (nmat, act, gather)
+    if _tile_height(cfg, counts) == 320:
+        return "k_grouped_gemm_lds<320, 320, %d, %d, %s>" % (nmat, act, gather)
+    return "k_grouped_gemm_pp<%d, %d, %s>" % (nmat, act, gather)
 
 
 def _roofline(kd, peak_flops):

@@ -397,12 +397,16 @@ __device__ __attribute__((always_inline)) inline void kstep(
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-    // issue order: one DMA instruction, then FM*FN/DPW MFMAs, DPW times
-    constexpr int PER = FM * FN / S::DPW > 0 ? FM * FN / S::DPW : 1;
+    // issue order: one DMA instruction, then FM*FN/DPW MFMAs, DPW times (not for the
+    // 320-row tile, whose 60 MFMAs and 9 DMA instructions do not pair evenly; there the
+    // pattern made the register allocator move accumulators every step)
+    if constexpr (BM != 320) {
+        constexpr int PER = FM * FN / S::DPW > 0 ? FM * FN / S::DPW : 1;
 #pragma unroll
-    for (int i = 0; i < S::DPW; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (the LDS DMA)
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // MFMA
+        for (int i = 0; i < S::DPW; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read (the LDS DMA)
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // MFMA
+        }
     }
 }
 
@@ -588,9 +592,10 @@ __device__ __forceinline__ void gemm_tiles(
     }
 }
 
-// The grouped GEMM kernel.  BMA and BMB are the row-tile heights the tile list may use
-// (equal for the 64- and 128-row kernels); the tile builder chose one from the actual
-// per-expert counts and stored it in ntiles_p[1], so one launch runs one shape.
+// The grouped GEMM kernel.  BMA and BMB are the row-tile heights the tile list may use;
+// the tile builder chose one from the actual per-expert counts and stored it in
+// ntiles_p[1].  A single-height instance (BMA == BMB) returns at once when the list was
+// built for another height (it is then the other half of a launch pair).
 template <int BMA, int BMB>
 struct LdsPair {
     template <int NMAT>
@@ -607,10 +612,316 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
     long long a_rows) {
     extern __shared__ uint4 smem[];
-    if (BMA != BMB && __builtin_amdgcn_readfirstlane(ntiles_p[1]) == BMB)
+    const int bm = __builtin_amdgcn_readfirstlane(ntiles_p[1]);
+    if (BMA == BMB && bm != BMA) return;      // the list is for the other kernel of the launch pair
+    if (BMA != BMB && bm == BMB)
         gemm_tiles<BMB, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
     else
         gemm_tiles<BMA, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+}
+
+// ------------------------------------------- ping-pong variant (two wavefront groups)
+// Same tiles, LDS layout and DMA as above, with 8 wavefronts per workgroup in two groups
+// of four (one wavefront of each group per SIMD, 128 accumulator registers each).  Each K
+// step has a read phase (DMA issue and fragment reads) and an MFMA phase; the groups run
+// them out of step, so one group's LDS reads and DMA issue overlap the other group's
+// MFMAs.  Between two consecutive barriers one group is in its read phase and the other
+// in its MFMA phase:
+//   group 0:  R0 | M0 | R1 | M1 | ... | M(KT-1) | (idle)
+//   group 1: (idle) | R0 | M0 | R1 | ... | R(KT-1) | M(KT-1)
+// Both groups therefore pass 2 KT + 1 barriers per item (plus the prologue's).
+//   * Stage k is read in group 0's phase 2k and group 1's phase 2k+1.  Every wavefront
+//     waits for its own DMA of stage k before barrier 2k-1 (group 0 at the end of M(k-1),
+//     group 1 at the end of R(k-1)), so all of stage k has landed when it is read.
+//   * R(k) starts the DMA of stage k+3 into the slot of stage k-1.  Each read phase ends
+//     with lgkmcnt(0) before its barrier, so both groups' reads of stage k-1 (phases 2k-2
+//     and 2k-1) are complete before either group issues that DMA (phases 2k and 2k+1).
+template <int BM, int NMAT>
+struct PpShape {
+    static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, BK = 32, NSTAGE = 4;
+    static constexpr int LBN = 256, LBNm = LBN / NMAT;
+    static constexpr int GM = BM / 2;                        // rows of one group
+    static constexpr int WTM = GM / 2, WTN = BN / 2;         // wavefront tile (2 x 2 per group)
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2, STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_INSTR = A_STAGE / 1024, B_INSTR = B_STAGE / 1024;
+    // A instruction j goes to wavefront j % 8: group 0 (wavefronts 0-3) may take one more
+    static constexpr int ADMA0 = (A_INSTR + 7 - 0) / 8, ADMA1 = (A_INSTR + 7 - 4) / 8;
+    static constexpr int BDMA = B_INSTR / 8;
+    static constexpr int DPW0 = ADMA0 + BDMA, DPW1 = ADMA1 + BDMA;
+    static constexpr int BROW = 2 * LBNm, CS_STRIDE = BNm + 8;
+    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
+                                            ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
+    static_assert(A_INSTR % 8 == 0 || A_INSTR % 8 == 4, "A instructions split by groups");
+    static_assert(B_INSTR % 8 == 0, "W instructions split evenly");
+};
+
+template <int ADMA, int BDMA>
+struct PpPlan {
+    uint32_t a_off[ADMA], a_k[ADMA], b_off[BDMA];
+};
+
+// This wavefront's share of one stage's DMA (ADMA A and BDMA W instructions).
+template <int BM, int NMAT, int ADMA>
+__device__ __forceinline__ void pp_dma(lds_char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                       __amdgpu_buffer_rsrc_t rb1, const PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& pl,
+                                       int kt, int K, uint32_t rowB, int wave) {
+    using S = PpShape<BM, NMAT>;
+    const uint32_t k0 = (uint32_t)kt * S::BK;
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i) {
+        const uint32_t off = (k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (wave + 8 * i) * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < S::BDMA; ++i) {
+        const int j = wave * S::BDMA + i;
+        const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && j >= 8) ? rb1 : rb0,
+                                                 (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+// DMA plan of one wavefront for one tile: A instruction j = wave + 8 i covers 16 rows x
+// 4 chunks; W instruction j = wave * BDMA + i as in the 4-wavefront kernel.
+template <int BM, int NMAT, int ADMA, bool GATHER>
+__device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& pl, const Tile& tl, int rows, int n0,
+                                        int K, int N, const int32_t* __restrict__ gather_rows, int wave, int lane) {
+    using S = PpShape<BM, NMAT>;
+    const uint32_t rowB = (uint32_t)N * 2;
+#pragma unroll
+    for (int i = 0; i < ADMA; ++i) {
+        const int r = (wave + 8 * i) * 16 + (lane >> 2);
+        const int q = (lane & 3) ^ swa4(r);
+        pl.a_k[i] = (uint32_t)(q * 8);
+        long long row = tl.row0 + min(r, rows - 1);
+        if constexpr (GATHER) row = gather_rows[row];
+        else row -= tl.row0;
+        pl.a_off[i] = (uint32_t)(row * K * 2) + (uint32_t)(q * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < S::BDMA; ++i) {
+        const int j = wave * S::BDMA + i;
+        int k, c;
+        if constexpr (NMAT == 1) {
+            k = j * 2 + (lane >> 5);
+            c = (lane & 31) ^ fk(k);
+        } else {
+            k = (j & 7) * 4 + (lane >> 4);
+            c = (lane & 15) ^ fk(k);
+        }
+        const uint32_t col = (uint32_t)(n0 + 8 * c);
+        pl.b_off[i] = (8 * c < S::BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
+    }
+}
+
+// The whole K loop of one work item for group GROUP: plan, prologue, loop.
+template <int GROUP, int BM, int NMAT, bool GATHER>
+__device__ __attribute__((always_inline)) inline void pp_item(
+    lds_char* lds, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
+    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
+    f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]);
+
+template <int BM, int NMAT>
+__device__ __forceinline__ void pp_read(const lds_char* st, int a_rd, int b_rd, int g, int wn,
+                                        bf16x8_t (&af)[PpShape<BM, NMAT>::FM],
+                                        bf16x8_t (&bfr)[PpShape<BM, NMAT>::FN]) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
+    const lds_char* Bs = st + S::A_STAGE;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(st + a_rd + fm * 16 * S::BK * 2);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        int mat, blk;
+        if constexpr (NMAT == 1) {
+            mat = 0;
+            blk = wn * (S::WTN / 16) + fn;
+        } else {
+            mat = fn < FN / 2 ? 0 : 1;
+            blk = wn * (FN / 2) + (fn % (FN / 2));
+        }
+        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (((blk & ~7) | ((blk & 7) ^ g)) << 5);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bfr[fn] = __builtin_bit_cast(bf16x8_t, v);
+    }
+}
+
+// The K loop of one group (see the phase table above).  `rows_here`: the wavefront has
+// rows of the tile (else it only moves its DMA share and keeps the barriers).
+template <int GROUP, int BM, int NMAT>
+__device__ __attribute__((always_inline)) inline void pp_kloop(
+    lds_char* lds, int KT, bool rows_here, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+    __amdgpu_buffer_rsrc_t rb1,
+    const PpPlan<GROUP == 0 ? PpShape<BM, NMAT>::ADMA0 : PpShape<BM, NMAT>::ADMA1, PpShape<BM, NMAT>::BDMA>& pl,
+    int K, uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn,
+    f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1;
+    constexpr int DPW = ADMA + S::BDMA;
+    constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE, FM = S::FM, FN = S::FN;
+    bf16x8_t af[FM], bfr[FN];
+    if constexpr (GROUP == 1) kloop_barrier();                  // group 1's idle first phase
+    for (int kt = 0; kt < KT; ++kt) {
+        // read phase: DMA of stage kt + 3 into the slot of stage kt - 1, fragments of stage kt
+        pp_dma<BM, NMAT, ADMA>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl, kt + NSTAGE - 1, K,
+                               rowB, wave);
+        if (rows_here) pp_read<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, a_rd, b_rd, g, wn, af, bfr);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (GROUP == 1) wait_dma<DPW>(2);              // stage kt + 1 complete
+        kloop_barrier();
+        // MFMA phase
+        if (rows_here) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+        }
+        // the accumulators live in AGPRs (at two wavefronts per SIMD the compiler would
+        // otherwise keep them in VGPRs, next to the fragments, and spill)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
+        if constexpr (GROUP == 0) wait_dma<DPW>(2);              // stage kt + 1 complete
+        kloop_barrier();
+    }
+    if constexpr (GROUP == 0) kloop_barrier();                  // group 0's idle last phase
+}
+
+template <int GROUP, int BM, int NMAT, bool GATHER>
+__device__ __attribute__((always_inline)) inline void pp_item(
+    lds_char* lds, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
+    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
+    f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1;
+    const uint32_t rowB = (uint32_t)N * 2;
+    PpPlan<ADMA, S::BDMA> pl;
+    pp_plan<BM, NMAT, ADMA, GATHER>(pl, tl, rows, n0, K, N, gather_rows, wave, lane);
+    // prologue: stages 0..2 in flight, stage 0 complete for all before the first reads
+#pragma unroll
+    for (int t = 0; t < S::NSTAGE - 1; ++t)
+        pp_dma<BM, NMAT, ADMA>(lds + t * S::STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
+    wait_dma<ADMA + S::BDMA>(2);
+    kloop_barrier();
+    pp_kloop<GROUP, BM, NMAT>(lds, KT, rows_here, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+}
+
+template <int BM, int NMAT, int ACT, bool GATHER>
+__device__ __forceinline__ void gemm_tiles_pp(
+    uint4* smem, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
+    long long a_rows) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int BNm = S::BNm, GM = S::GM, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
+    constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, NSTAGE = S::NSTAGE, CS_STRIDE = S::CS_STRIDE;
+    constexpr int BROW = S::BROW, ADMA0 = S::ADMA0, ADMA1 = S::ADMA1, BDMA = S::BDMA;
+    static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
+    lds_char* lds = (lds_char*)smem;
+    bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wsub = (wave >> 1) & 1, wn = wave & 1;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int row0 = grp * GM + wsub * WTM;                      // first tile row of this wavefront
+
+    const int NT = (N + BNm - 1) / BNm;
+    const int KT = (K + BK - 1) / BK;
+    const long long total = (long long)(*ntiles_p) * NT;
+    const int G = gridDim.x;
+    const long long first = (long long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t rowB = (uint32_t)N * 2;
+    const int a_rd = (row0 + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+    const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);
+    const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
+
+    for (long long w = first; w < total; w += G) {
+        const Tile te = tiles[w / NT];
+        const long long local = w - (long long)te.first * NT;
+        const int nt = (int)(local / te.cnt);
+        const Tile tl = tiles[te.first + (int)(local % te.cnt)];
+        const int rows = tl.row1 - tl.row0;
+        const int n0 = nt * BNm;
+        const bool rows_here = rows > row0;
+
+        const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, (uint32_t)(a_rows * K * 2))
+                                                 : make_rsrc(A + (long long)tl.row0 * K, (uint32_t)rows * K * 2);
+        const long long eoff = (long long)tl.e * K * N;
+        const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + eoff, (uint32_t)K * rowB);
+        const __amdgpu_buffer_rsrc_t rb1 = make_rsrc((NMAT == 2 ? B1 : B0) + eoff, (uint32_t)K * rowB);
+
+        f32x4_t acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        if (grp == 0)
+            pp_item<0, BM, NMAT, GATHER>(lds, KT, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows, wave,
+                                         lane, a_rd, b_rd, g, wn, acc);
+        else
+            pp_item<1, BM, NMAT, GATHER>(lds, KT, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows, wave,
+                                         lane, a_rd, b_rd, g, wn, acc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
+        __syncthreads();
+
+        constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
+        if (rows_here) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fo = 0; fo < FO; ++fo) {
+                    const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float val = acc[fm][fo][v];
+                        if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
+                        else if constexpr (ACT == 1) val = silu_f32(val);
+                        const int r = row0 + 16 * fm + 4 * lq + v;
+                        sC[r * CS_STRIDE + col] = f32_to_bf16(val);
+                    }
+                }
+        }
+        __syncthreads();
+        constexpr int CPR = BNm / 8;
+        for (int c = tid; c < rows * CPR; c += 512) {
+            const int r = c / CPR, cc = c % CPR;
+            const int col = n0 + cc * 8;
+            if (col < N)
+                *reinterpret_cast<uint4*>(C + (long long)(tl.row0 + r) * N + col) =
+                    *reinterpret_cast<const uint4*>(sC + r * CS_STRIDE + cc * 8);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+}
+
+template <int NMAT>
+constexpr size_t pp_lds_bytes() { return PpShape<256, NMAT>::LDS_BYTES; }
+
+// 256-row grouped GEMM, ping-pong form (512 threads).  It is launched together with the
+// 320-row kernel; whichever height the tile builder chose runs, the other returns.  (The
+// ping-pong form is faster where operands mostly hit in L2; on the weight stream from HBM
+// of 320-row tiles, whose reads come half a step later than in the 4-wavefront kernel,
+// it was slower.)
+template <int NMAT, int ACT, bool GATHER>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm_pp(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
+    long long a_rows) {
+    extern __shared__ uint4 smem[];
+    if (__builtin_amdgcn_readfirstlane(ntiles_p[1]) != 256) return;
+    gemm_tiles_pp<256, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
 }
 
 // ------------------------------------------------------------------------ tile list
@@ -710,13 +1021,13 @@ hipError_t launch_build_tiles_for(const int32_t* offsets, int E, GemmCfg cfg, in
 // rounded to a multiple of 8 (the XCD count) and capped by the work-item bound.
 template <typename KernT>
 static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int& occ_cache,
-                                  long long max_items, unsigned& grid) {
+                                  long long max_items, unsigned& grid, int threads = 256) {
     if (!ready) {   // per process: properties of the code object
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds_bytes);
         if (e != hipSuccess) return e;
         int occ = 1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, lds_bytes) != hipSuccess || occ < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, lds_bytes) != hipSuccess || occ < 1)
             occ = 1;
         occ_cache = occ;
         ready = true;
@@ -745,6 +1056,26 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), S::LDS_BYTES, st, (const bf16_t*)A, gather_rows,
                            (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N);
     } else {
+        if constexpr (BM == 256 && BMB == 320) {
+            // launch pair: 256-row tiles in the ping-pong kernel, 320-row tiles in the
+            // 4-wavefront kernel; the one whose height was not chosen returns at once
+            static bool ready2 = false;
+            static int occ2 = 1;
+            constexpr size_t pp_bytes = pp_lds_bytes<NMAT>();
+            auto kpp = k_grouped_gemm_pp<NMAT, ACT, GATHER>;
+            hipError_t e = persistent_grid(kpp, pp_bytes, ready2, occ2, max_items, G, 512);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows,
+                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            constexpr size_t lds_bytes = LdsShape<320, NMAT>::LDS_BYTES;
+            auto kern = k_grouped_gemm_lds<320, 320, NMAT, ACT, GATHER>;
+            e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
+                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
+            return hipGetLastError();
+        }
         constexpr size_t lds_bytes = LdsPair<BM, BMB>::template bytes<NMAT>();
         auto kern = k_grouped_gemm_lds<BM, BMB, NMAT, ACT, GATHER>;
         hipError_t e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
