@@ -8,9 +8,11 @@ workload is the pages' worked shape: 8192 tokens (batch 4 x seq 2048), hidden 40
 64 experts, top-2, two-layer SiLU FFN 4096 -> 16384 -> 4096, bf16 with fp32 routing.
 
 Prints one JSON line: tokens/s, the roofline figures of the dominant grouped-GEMM kernel
-(timed live with HIP events that moe_forward records around each projection's launch on
-its stream; the other projection is reported beside it) and the CPU oracle timed on a
-bounded sample of the same workload.
+(timed live with HIP events that moe_forward records at its stage boundaries on its
+stream; the other projection is reported beside it), per-stage times and rates, the
+layer time's median and p10/p90 with and without a 256 MB MALL flush before each step,
+peak rates measured on this GPU (bf16 MFMA loop, HBM read and copy) beside the published
+ones, and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -33,10 +35,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="pages_worked_shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1536,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--flush-steps", type=int, default=5,
+                    help="extra steps, each after a 1 GiB write that evicts the MALL (0: none)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak-rate microbenchmarks")
     return ap.parse_args()
 
 
@@ -90,25 +95,50 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-    for trio in ev:              # materialise the event handles
-        for e in trio:
-            e.record()
+    NS = _lib.MOE_STAGE_EVENTS
+
+    def new_events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(NS)] for _ in range(n)]
+        for row in evs:          # materialise the event handles
+            for e in row:
+                e.record()
+        return evs
+
+    ev = new_events(K)
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     for i in range(K):
-        _lib.set_ffn_events(*ev[i])
+        _lib.set_stage_events(ev[i])
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.set_ffn_events()
+    _lib.set_stage_events(None)
 
     ms_step = (t1 - t0) * 1e3 / K
-    up_ms = float(np.mean([a.elapsed_time(m) for a, m, _ in ev]))
-    down_ms = float(np.mean([m.elapsed_time(c) for _, m, c in ev]))
+    # stage durations per step: [route, group, ffn up, ffn down, combine]
+    per = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(NS - 1)] for row in ev])
+    layer = np.array([row[0].elapsed_time(row[-1]) for row in ev])
+    up_ms = float(per[:, 2].mean())
+    down_ms = float(per[:, 3].mean())
     ffn_ms = up_ms + down_ms
     tokens_per_s = cfg.T * K / (t1 - t0)
+
+    # the same steps after a 1 GiB write each, so x and the routing tensors start out of the
+    # 256 MB MALL (not part of the timed loop above)
+    flushed = None
+    if args.flush_steps > 0:
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evf = new_events(args.flush_steps)
+        torch.cuda.synchronize()
+        for i in range(args.flush_steps):
+            junk.fill_(i & 0xFF)
+            _lib.set_stage_events(evf[i])
+            step()
+        torch.cuda.synchronize()
+        _lib.set_stage_events(None)
+        flushed = _spread([row[0].elapsed_time(row[-1]) for row in evf])
+        del junk
 
     sb = A.stage_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.ffn, cfg.dtype, touched)
     flops = A.ffn_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn)
@@ -134,6 +164,20 @@ def main():
     t_ffn_roof = max(flops / peak_flops, (sb.ffn_up + sb.ffn_down) / A.PEAK_HBM_BPS)
     sec = ffn_ms * 1e-3
 
+    def hbm_stage(ms, nbytes):
+        return {"ms": ms, "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                "pct_hbm_peak": nbytes / (ms * 1e-3) / A.PEAK_HBM_BPS * 100}
+
+    stages = {
+        "route": dict(hbm_stage(float(per[:, 0].mean()), sb.route),
+                      gate_tflops=A.gate_flops(cfg.T, cfg.H, cfg.E) / (per[:, 0].mean() * 1e-3) / 1e12),
+        "group": hbm_stage(float(per[:, 1].mean()), sb.group),
+        "ffn_up": dict(hbm_stage(up_ms, sb.ffn_up), tflops=kernels["up"]["flops"] / (up_ms * 1e-3) / 1e12),
+        "ffn_down": dict(hbm_stage(down_ms, sb.ffn_down),
+                         tflops=kernels["down"]["flops"] / (down_ms * 1e-3) / 1e12),
+        "combine": hbm_stage(float(per[:, 4].mean()), sb.combine),
+    }
+
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -148,12 +192,95 @@ def main():
         "grouped_ffn_pct_roofline": t_ffn_roof / sec * 100,
         "touched_experts": touched,
         "roofline": roof,
+        "layer_ms": _spread(layer.tolist()),
+        "layer_ms_mall_flushed": flushed,
+        "stages": stages,
+        "measured_peaks": None if args.no_peaks else measured_peaks(dev),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _spread(ms):
+    """Median and 10th/90th percentiles of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def measured_peaks(dev):
+    """Peak rates measured on this GPU with the library's microbenchmark kernels, beside
+    the published MI355X figures the roofline uses (best of several runs each)."""
+    import torch
+    from mixture_experts_layer_46_amd import _lib
+    from mixture_experts_layer_46_amd import accounting as A
+
+    def timed(fn, reps):
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 2 * cus, 1000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    khz = _lib.peak_mfma_bf16(blocks, 10, sink, clocks)            # warm-up
+    t = timed(lambda: _lib.peak_mfma_bf16(blocks, iters, sink, clocks), 3)
+    flops = blocks * 4 * iters * 32 * 16384
+    cyc, ticks = (int(v) for v in clocks.cpu())
+    clock_ghz = cyc / (ticks / (khz * 1e3)) / 1e9 if ticks > 0 and khz > 0 else None
+
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    rblocks = 8 * cus
+    rsink = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
+    _lib.peak_hbm_read(buf, n, rblocks, rsink)
+    t_read = timed(lambda: _lib.peak_hbm_read(buf, n, rblocks, rsink), 5)
+    half = n // 2
+    src, dst = buf[:half], buf[half:]
+    t_copy = timed(lambda: _lib.peak_hbm_copy(src, dst, half, rblocks), 5)
+    del buf
+    return {"bf16_mfma_tflops": flops / t / 1e12,
+            "mfma_loop_clock_ghz": clock_ghz,
+            "hbm_read_GBps": n / t_read / 1e9,
+            "hbm_copy_GBps": 2 * half / t_copy / 1e9,
+            "published": {"bf16_mfma_tflops": A.PEAK_BF16_FLOPS / 1e12, "hbm_GBps": A.PEAK_HBM_BPS / 1e9},
+            "how": f"MFMA-only loop {blocks} workgroups x {iters} x 32 MFMA per wavefront; "
+                   f"4 GiB streaming read and 2 GiB copy (read + write bytes), {rblocks} workgroups; "
+                   "best of 3 / 5 runs"}
+
+
+def _host_info():
+    """CPU model, usable cores and RAM of the host."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    ram = None
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal:"):
+                ram = int(line.split()[1]) / (1 << 20)
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "host_ram_gib": ram}
 
 
 def _tile_height(cfg, counts) -> int:
@@ -262,7 +389,7 @@ def cpu_baseline(cfg, inp, n_tokens):
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt, **_host_info(),
             "sample": f"first {n_tokens} tokens of {cfg.name} ({len(used)} experts touched), "
                       f"numpy float64, experts streamed and widened to fp64 one at a time"}
 

@@ -173,14 +173,22 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
                             const int32_t* counts, const int32_t* offsets, float* stats,
                             hipStream_t stream);
 
-/* Timing hook for benchmarks.  When all three events are non-NULL, later moe_forward
- * calls made by the calling thread record, on their stream, `up_start` just before the
- * launch of the first expert projection (w_in, and w_up for SwiGLU), `mid` between it and
- * the launch of the second projection (w_out), and `down_stop` just after that one, so
- * the caller can read each projection kernel's duration with hipEventElapsedTime.  The
- * events are the caller's (created with timing enabled); all NULL switches the hook off,
- * a mix of NULL and non-NULL is MOE_ERR_NULL.  Host only. */
-moe_status moe_set_ffn_events(hipEvent_t up_start, hipEvent_t mid, hipEvent_t down_stop);
+/* Timing hook for benchmarks.  With `events` pointing to MOE_STAGE_EVENTS events (the
+ * caller's, created with timing enabled) and n == MOE_STAGE_EVENTS, later moe_forward
+ * calls made by the calling thread record them on their stream at the stage boundaries:
+ *   [0] before the gate projection
+ *   [1] after top-k and gates (the routing stage, [FourStage §2.1-§2.2])
+ *   [2] after the grouping (histogram, offsets, maps, the GEMM tile list, [Principles §5.1]),
+ *       i.e. just before the launch of the first expert projection (w_in, and w_up)
+ *   [3] between the two expert projections (before the w_out launch)
+ *   [4] after the second projection
+ *   [5] after the combine ([FourStage §2.4])
+ * so hipEventElapsedTime between neighbours gives each stage's duration, and [2]-[3],
+ * [3]-[4] each projection kernel's.  events == NULL with n == 0 switches the hook off.
+ * A NULL array with n != 0 or a NULL entry is MOE_ERR_NULL; any other n is
+ * MOE_ERR_SHAPE.  The array is copied; host only. */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_set_stage_events(const hipEvent_t* events, int n);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);

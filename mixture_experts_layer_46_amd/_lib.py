@@ -23,8 +23,10 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_router_stats", "moe_set_ffn_events", "moe_status_str",
-           "moe_last_error"]
+           "moe_forward", "moe_router_stats", "moe_set_stage_events", "moe_status_str",
+           "moe_last_error", "moe_peak_mfma_bf16", "moe_peak_hbm_read", "moe_peak_hbm_copy"]
+
+MOE_STAGE_EVENTS = 6
 
 
 class MoeShape(ctypes.Structure):
@@ -68,8 +70,14 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.moe_set_ffn_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.moe_set_ffn_events.restype = ctypes.c_int
+    lib.moe_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.moe_set_stage_events.restype = ctypes.c_int
+    lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.POINTER(ctypes.c_int), st]
+    lib.moe_peak_mfma_bf16.restype = ctypes.c_int
+    lib.moe_peak_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, st]
+    lib.moe_peak_hbm_read.restype = ctypes.c_int
+    lib.moe_peak_hbm_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, st]
+    lib.moe_peak_hbm_copy.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
@@ -174,9 +182,31 @@ def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None
                                                        _stream(stream)))
 
 
-def set_ffn_events(up_start=None, mid=None, down_stop=None):
-    """Record torch.cuda.Event objects before the first expert projection, between the
-    two projections and after the second, in later forward calls on this thread (no
-    arguments switches it off)."""
-    ev = [None if e is None else e.cuda_event for e in (up_start, mid, down_stop)]
-    _check("moe_set_ffn_events", load().moe_set_ffn_events(*ev))
+def set_stage_events(events=None):
+    """Record MOE_STAGE_EVENTS torch.cuda.Event objects at the stage boundaries of later
+    forward calls on this thread: before routing, after routing, after grouping (= before
+    the first expert projection), between the projections, after the second projection,
+    after the combine.  None switches it off."""
+    if events is None:
+        _check("moe_set_stage_events", load().moe_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("moe_set_stage_events", load().moe_set_stage_events(arr, len(events)))
+
+
+def peak_mfma_bf16(blocks: int, iters: int, sink, clocks, stream=None) -> int:
+    """Enqueue the MFMA-only loop; returns the constant clock's rate in kHz."""
+    khz = ctypes.c_int(0)
+    _check("moe_peak_mfma_bf16", load().moe_peak_mfma_bf16(blocks, iters, _ptr(sink), _ptr(clocks),
+                                                           ctypes.byref(khz), _stream(stream)))
+    return khz.value
+
+
+def peak_hbm_read(src, nbytes: int, blocks: int, sink, stream=None):
+    _check("moe_peak_hbm_read", load().moe_peak_hbm_read(_ptr(src), nbytes, blocks, _ptr(sink),
+                                                         _stream(stream)))
+
+
+def peak_hbm_copy(src, dst, nbytes: int, blocks: int, stream=None):
+    _check("moe_peak_hbm_copy", load().moe_peak_hbm_copy(_ptr(src), _ptr(dst), nbytes, blocks,
+                                                         _stream(stream)))

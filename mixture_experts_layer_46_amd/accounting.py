@@ -61,7 +61,8 @@ def expert_weight_bytes(H: int, F: int, ffn: str, dtype: str) -> int:
 class StageBytes:
     """Algorithmic HBM bytes of each stage, given the number of experts touched."""
     route: int
-    permute: int
+    permute: int       # the explicit grouping with the row gather (moe_permute with x)
+    group: int         # moe_forward's grouping: top-k indices in, the two maps out
     ffn_up: int        # first grouped GEMM: touched W_in (+W_up) + x once + h out
     ffn_down: int      # second grouped GEMM: touched W_out + h in + y rows out
     combine: int
@@ -78,6 +79,7 @@ def stage_bytes(T: int, H: int, E: int, k: int, F: int, ffn: str, dtype: str,
     w_down_side = F * H * b * touched
     ffn_up = w_up_side + T * H * b + P * F * b      # rows are gathered from x itself
     ffn_down = w_down_side + P * F * b + P * H * b
+    group = P * 4 + P * 8
     combine = P * H * b + T * H * b + P * 8
     layer = w_up_side + w_down_side + 2 * T * H * b
-    return StageBytes(route, permute, ffn_up, ffn_down, combine, layer)
+    return StageBytes(route, permute, group, ffn_up, ffn_down, combine, layer)

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "peaks.hip"]
 ARCH = "gfx950"
 
 

@@ -16,8 +16,9 @@ namespace moe {
 namespace {
 
 thread_local std::string g_last_error;
-// timing hook of moe_set_ffn_events: {before up, between, after down}, or all NULL
-thread_local hipEvent_t g_ffn_ev[3] = {nullptr, nullptr, nullptr};
+// timing hook of moe_set_stage_events: the stage boundaries of moe_forward, or off
+thread_local hipEvent_t g_stage_ev[MOE_STAGE_EVENTS] = {};
+thread_local bool g_stage_on = false;
 
 moe_status fail(moe_status st, const char* fmt, ...) {
     char buf[512];
@@ -163,6 +164,8 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
 
 }  // namespace
 
+moe_status report_error(moe_status st, const char* text) { return fail(st, "%s", text); }
+
 int device_cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -300,17 +303,22 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     int32_t* sorted_token = at<int32_t>(workspace, L.sorted_token);
     int32_t* row_of_pair = at<int32_t>(workspace, L.row_of_pair);
     const int splits = gate_splits(s.T, s.H, s.E);
+    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[0], stream), "stage event");
     HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, stream), "gate_logits");
     HIPCHK(launch_topk(logits, splits, nullptr, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");
+    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[1], stream), "stage event");
     HIPCHK(launch_group(idx, P, s.k, s.E, s.capacity, at<int32_t>(workspace, L.segcnt),
                         at<int32_t>(workspace, L.counts), offsets, sorted_token, row_of_pair, stream),
            "group");
-    // the first projection reads x rows through sorted_token: no x_perm copy
+    // the first projection reads x rows through sorted_token: no x_perm copy.  Stage
+    // events 2..4 are recorded by the grouped FFN (before, between and after its two
+    // projections; the tile list is built before event 2).
     st = run_grouped(s, x, sorted_token, offsets, w_in, w_up, w_out, at<void>(workspace, L.y),
-                     workspace, g_ffn_ev[0] ? g_ffn_ev : nullptr, stream);
+                     workspace, g_stage_on ? g_stage_ev + 2 : nullptr, stream);
     if (st != MOE_OK) return st;
     HIPCHK(launch_combine(at<void>(workspace, L.y), row_of_pair, gw, out, s.T, s.k, s.H, s.dtype, stream),
            "combine");
+    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[5], stream), "stage event");
     return MOE_OK;
 }
 
@@ -333,12 +341,17 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
     return MOE_OK;
 }
 
-moe_status moe_set_ffn_events(hipEvent_t up_start, hipEvent_t mid, hipEvent_t down_stop) {
-    const int given = (up_start != nullptr) + (mid != nullptr) + (down_stop != nullptr);
-    if (given != 0 && given != 3) return fail(MOE_ERR_NULL, "give all three events or none");
-    g_ffn_ev[0] = up_start;
-    g_ffn_ev[1] = mid;
-    g_ffn_ev[2] = down_stop;
+moe_status moe_set_stage_events(const hipEvent_t* events, int n) {
+    if (events == nullptr && n == 0) {
+        g_stage_on = false;
+        return MOE_OK;
+    }
+    if (events == nullptr) return fail(MOE_ERR_NULL, "events is NULL with n = %d", n);
+    if (n != MOE_STAGE_EVENTS) return fail(MOE_ERR_SHAPE, "n = %d, expected %d events", n, MOE_STAGE_EVENTS);
+    for (int i = 0; i < n; ++i)
+        if (events[i] == nullptr) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
+    for (int i = 0; i < n; ++i) g_stage_ev[i] = events[i];
+    g_stage_on = true;
     return MOE_OK;
 }
 

@@ -9,6 +9,10 @@
 
 namespace moe {
 
+// Sets the calling thread's moe_last_error() text and returns st (for entry points
+// defined outside api.hip).
+moe_status report_error(moe_status st, const char* text);
+
 // pairs per segment of the grouping kernels (one wavefront handles one segment)
 constexpr int kSeg = 512;
 

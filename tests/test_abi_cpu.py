@@ -1,5 +1,6 @@
-"""The C ABI library on the host: it loads, exports every symbol include/moe.h declares,
-and rejects bad arguments before anything reaches a GPU (no compute calls here)."""
+"""The C ABI library on the host: it loads, exports every symbol the headers under
+include/ declare, and rejects bad arguments before anything reaches a GPU (no compute
+calls here)."""
 import ctypes
 import os
 import re
@@ -9,7 +10,8 @@ import pytest
 from mixture_experts_layer_46_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 FAKE = 1 << 40          # a 16-byte aligned address that is never dereferenced
 MIS = FAKE + 8          # misaligned
@@ -23,9 +25,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -145,3 +149,30 @@ def test_capacity_rows():
     assert _lib.capacity_rows(None, 8192, 2, 64) == 0
     assert _lib.capacity_rows(1.0, 8192, 2, 64) == 256
     assert _lib.capacity_rows(1.25, 8192, 2, 64) == 320
+
+
+def test_stage_events_argument_checks(lib):
+    arr = (ctypes.c_void_p * 6)(*([FAKE] * 6))
+    assert lib.moe_set_stage_events(None, 6) == 1                 # NULL array
+    assert lib.moe_set_stage_events(arr, 5) == 2                  # wrong count
+    bad = (ctypes.c_void_p * 6)(*([FAKE] * 5 + [None]))
+    assert lib.moe_set_stage_events(bad, 6) == 1                  # NULL entry
+    assert b"events[5]" in lib.moe_last_error()
+    assert lib.moe_set_stage_events(arr, 6) == 0                  # stored, nothing recorded yet
+    assert lib.moe_set_stage_events(None, 0) == 0                 # and switched off again
+
+
+def test_peak_entry_points_argument_checks(lib):
+    khz = ctypes.c_int(0)
+    assert lib.moe_peak_mfma_bf16(256, 10, None, FAKE, ctypes.byref(khz), None) == 1
+    assert lib.moe_peak_mfma_bf16(0, 10, FAKE, FAKE, None, None) == 2
+    assert lib.moe_peak_mfma_bf16(256, 0, FAKE, FAKE, None, None) == 2
+    assert lib.moe_peak_mfma_bf16(256, 10, MIS, FAKE, None, None) == 4
+    assert lib.moe_peak_hbm_read(None, 1 << 20, 256, FAKE, None) == 1
+    assert lib.moe_peak_hbm_read(FAKE, (1 << 20) + 4, 256, FAKE, None) == 2
+    assert lib.moe_peak_hbm_read(FAKE, 0, 256, FAKE, None) == 2
+    assert lib.moe_peak_hbm_read(FAKE, 1 << 20, 70000, FAKE, None) == 2
+    assert lib.moe_peak_hbm_read(MIS, 1 << 20, 256, FAKE, None) == 4
+    assert lib.moe_peak_hbm_copy(FAKE, None, 1 << 20, 256, None) == 1
+    assert lib.moe_peak_hbm_copy(FAKE, FAKE + (1 << 19), 1 << 20, 256, None) == 2   # overlap
+    assert b"overlap" in lib.moe_last_error()
