@@ -276,6 +276,14 @@ typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Zeroes one accumulator as a value of its own: with a zero constant shared by several
+// accumulators, the register allocator may not update them in place in the K loop and
+// then moves accumulators at every step.
+__device__ __forceinline__ void acc_zero(f32x4_t& a) {
+    a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    asm volatile("" : "+a"(a));
+}
+
 __device__ __forceinline__ int fk(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 // A-row swizzle: 16-byte chunk q of tile row m sits at slot q ^ swa4(m).  On gfx950 a
 // ds_read_b128 serves 16 lanes per LDS cycle (64 banks), grouped by bit2^bit3^bit4 of
@@ -358,7 +366,7 @@ __device__ __attribute__((always_inline)) inline void kstep(
     __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int kt_dma, int K, uint32_t rowB,
     int wave, int a_rd, int b_rd, int g, int wn,
-    f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
+    f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN]) {
     using S = LdsShape<BM, NMAT>;
     constexpr int FM = FMA, FN = S::FN, BROW = S::BROW;
     const lds_char* As = cur;
@@ -419,7 +427,7 @@ template <int BM, int NMAT, int FMA>
 __device__ __attribute__((always_inline)) inline void kloop(
     lds_char* lds, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K, uint32_t rowB, int wave,
-    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[LdsShape<BM, NMAT>::FM][LdsShape<BM, NMAT>::FN]) {
+    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN]) {
     using S = LdsShape<BM, NMAT>;
     constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE;
     for (int kt = 0; kt < KT; ++kt) {
@@ -437,6 +445,47 @@ __device__ __attribute__((always_inline)) inline void kloop(
 // otherwise leads the compiler to drain every DMA in flight (vmcnt(0)) at each step; the
 // memory clobber still keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The rows part of one work item for a wavefront whose rows fill FMA 16-row blocks: the
+// K loop into accumulators of exactly those blocks, then (after the workgroup barrier
+// that frees the LDS stages) the activation and the bf16 rounding of its rows into the
+// output staging tile.  Each variant owns its accumulators, so the register allocator
+// never sees accumulators of one variant live in another.  Barriers: KT + 1, as in the
+// DMA-only path of a wavefront without rows.
+template <int BM, int NMAT, int ACT, int FMA>
+__device__ __attribute__((always_inline)) inline void rows_item(
+    lds_char* lds, bf16_t* sC, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+    __amdgpu_buffer_rsrc_t rb1, const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K,
+    uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn, int rb, int wrows, int lq, int l16) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int FN = S::FN, FO = (NMAT == 2) ? FN / 2 : FN, BNm = S::BNm, WTN = S::WTN;
+    f32x4_t acc[FMA][FN];
+#pragma unroll
+    for (int i = 0; i < FMA; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc_zero(acc[i][j]);
+    kloop<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < FMA; ++fm) {
+        // only this wavefront's row blocks (with the even split of a 320-row tile, the
+        // blocks past them are the other wavefront's rows)
+        if (16 * fm >= wrows) break;
+#pragma unroll
+        for (int fo = 0; fo < FO; ++fo) {
+            const int col = (NMAT == 2 ? wn * (BNm / S::WAVES_N) : wn * WTN) + 16 * fo + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float val = acc[fm][fo][v];
+                if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
+                else if constexpr (ACT == 1) val = silu_f32(val);
+                const int r = rb + 16 * fm + 4 * lq + v;
+                sC[r * S::CS_STRIDE + col] = f32_to_bf16(val);
+            }
+        }
+    }
+}
 
 // Wait until at most `pending` K steps' DMA of this wavefront are still in flight.
 template <int DPW>
@@ -491,7 +540,14 @@ __device__ __forceinline__ void gemm_tiles(
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
-        const bool wave_rows = rows > wm * WTM;
+        // 320-row tiles split the tile's rows evenly between the two wavefront rows (at a
+        // multiple of 16, so the A swizzle is unchanged): an expert with 256 rows then
+        // multiplies 8 row blocks per wavefront instead of 10 and 6
+        const int rsplit = BM == 320 ? min(WTM, (rows + 31) / 32 * 16) : WTM;
+        const int rb = wm * rsplit;                   // this wavefront's first row
+        const int wrows = min(rows - rb, rsplit);     // and its number of rows
+        const bool wave_rows = wrows > 0;
+        const int a_rd_item = a_rd + (rb - wm * WTM) * (BK * 2);
 
         DmaPlan<ADMA, BDMA> pl;
         // A: instruction i of this wavefront covers 16 rows x 4 chunks; lane -> (row, chunk)
@@ -528,28 +584,23 @@ __device__ __forceinline__ void gemm_tiles(
             pl.b_off[i] = (8 * c < BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
         }
 
-        f32x4_t acc[FM][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
         // prologue: steps 0..NSTAGE-2 in flight (steps past K read zeros, see kstep)
 #pragma unroll
         for (int t = 0; t < NSTAGE - 1; ++t)
             dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
         if (wave_rows) {
-            // a short expert fills only the first blocks of the wavefront tile: multiply
-            // just those (1, 2 or 4 blocks of 16 rows, else all)
-            const int wrows = rows - wm * WTM;
-            if (wrows <= 16)
-                kloop<BM, NMAT, 1>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
-            else if (FM > 2 && wrows <= 32)
-                kloop<BM, NMAT, (FM > 2 ? 2 : FM)>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
-            else if (FM > 4 && wrows <= 64)
-                kloop<BM, NMAT, (FM > 4 ? 4 : FM)>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
-            else
-                kloop<BM, NMAT, FM>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+            // a wavefront whose rows fill only the first blocks of its tile multiplies just
+            // those (1, 2, 4, and for 320-row tiles 8 or 9 blocks of 16 rows, else all)
+            const int ar = a_rd_item;
+#define MOE_ROWS_ITEM(F_) rows_item<BM, NMAT, ACT, (F_)>(lds, sC, KT, ra, rb0, rb1, pl, K, rowB, wave, ar, \
+                                                           b_rd, g, wn, rb, wrows, lq, l16)
+            if (wrows <= 16) MOE_ROWS_ITEM(1);
+            else if (FM > 2 && wrows <= 32) MOE_ROWS_ITEM(FM > 2 ? 2 : FM);
+            else if (FM > 4 && wrows <= 64) MOE_ROWS_ITEM(FM > 4 ? 4 : FM);
+            else if (BM == 320 && wrows <= 128) MOE_ROWS_ITEM(BM == 320 ? 8 : FM);
+            else if (BM == 320 && wrows <= 144) MOE_ROWS_ITEM(BM == 320 ? 9 : FM);
+            else MOE_ROWS_ITEM(FM);
+#undef MOE_ROWS_ITEM
         } else {       // no rows for this wavefront: it still moves its share of the tiles
             for (int kt = 0; kt < KT; ++kt) {
                 wait_dma<S::DPW>(NSTAGE - 2);
@@ -557,26 +608,8 @@ __device__ __forceinline__ void gemm_tiles(
                 dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
                                    kt + NSTAGE - 1, K, rowB, wave);
             }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
-        __syncthreads();
-
-        constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
-        if (wave_rows) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fo = 0; fo < FO; ++fo) {
-                    const int col = (NMAT == 2 ? wn * (BNm / WAVES_N) : wn * WTN) + 16 * fo + l16;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float val = acc[fm][fo][v];
-                        if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
-                        else if constexpr (ACT == 1) val = silu_f32(val);
-                        const int r = wm * WTM + 16 * fm + 4 * lq + v;
-                        sC[r * CS_STRIDE + col] = f32_to_bf16(val);
-                    }
-                }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
         }
         __syncthreads();
         constexpr int CPR = BNm / 8;
@@ -1075,13 +1108,14 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
             hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
                                (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
             return hipGetLastError();
+        } else {
+            constexpr size_t lds_bytes = LdsPair<BM, BMB>::template bytes<NMAT>();
+            auto kern = k_grouped_gemm_lds<BM, BMB, NMAT, ACT, GATHER>;
+            hipError_t e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
+                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
         }
-        constexpr size_t lds_bytes = LdsPair<BM, BMB>::template bytes<NMAT>();
-        auto kern = k_grouped_gemm_lds<BM, BMB, NMAT, ACT, GATHER>;
-        hipError_t e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
-                           (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
     }
     return hipGetLastError();
 }
