@@ -40,6 +40,27 @@
 
 namespace moe {
 
+// Work item w of a persistent grouped-GEMM launch -> (row tile mt, column block nt).
+// Items are expert-major.  Within an expert, its row tiles are taken in groups of
+// kItemRows and each group is walked column block by column block, so the items that
+// run at the same time (consecutive ones, on one XCD) cover a few row tiles x several
+// column blocks: each row tile's A operand is shared by several concurrent items and
+// each weight slice by the group's row tiles, instead of every A tile being re-read
+// for every column block when an expert has many row tiles.  An expert with at most
+// kItemRows row tiles is walked column block by column block over all of them.
+constexpr int kItemRows = 4;
+
+__device__ __forceinline__ void item_coords(long long w, int NT, const Tile* __restrict__ tiles, int& mt,
+                                            int& nt) {
+    const Tile te = tiles[w / NT];
+    const long long local = w - (long long)te.first * NT;           // < cnt * NT
+    const int rg = (int)(local / ((long long)kItemRows * NT));      // row-tile group
+    const int rows_in = min(kItemRows, te.cnt - rg * kItemRows);    // row tiles in this group
+    const int j = (int)(local - (long long)rg * kItemRows * NT);
+    nt = j / rows_in;
+    mt = te.first + rg * kItemRows + j % rows_in;
+}
+
 constexpr int BK = 64;
 
 __device__ __forceinline__ int swz(int n) { return ((n >> 1) ^ (n >> 4)) & 7; }
@@ -108,13 +129,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     }
 
     for (long long w = first; w < total; w += G) {
-        // decode the work item
-        // items are expert-major, then column block, then the expert's row tiles, so all
-        // row tiles sharing one weight slice are consecutive (one XCD, one L2)
-        const Tile te = tiles[w / NT];
-        const long long local = w - (long long)te.first * NT;
-        const int nt = (int)(local / te.cnt);
-        const int mt = te.first + (int)(local % te.cnt);
+        // decode the work item (order: item_coords)
+        int mt, nt;
+        item_coords(w, NT, tiles, mt, nt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
@@ -531,12 +548,9 @@ __device__ __forceinline__ void gemm_tiles(
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
 
     for (long long w = first; w < total; w += G) {
-        // items are expert-major, then column block, then the expert's row tiles, so all
-        // row tiles sharing one weight slice are consecutive (one XCD, one L2)
-        const Tile te = tiles[w / NT];
-        const long long local = w - (long long)te.first * NT;
-        const int nt = (int)(local / te.cnt);
-        const int mt = te.first + (int)(local % te.cnt);
+        // decode the work item (order: item_coords)
+        int mt, nt;
+        item_coords(w, NT, tiles, mt, nt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
@@ -878,10 +892,9 @@ __device__ __forceinline__ void gemm_tiles_pp(
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
 
     for (long long w = first; w < total; w += G) {
-        const Tile te = tiles[w / NT];
-        const long long local = w - (long long)te.first * NT;
-        const int nt = (int)(local / te.cnt);
-        const Tile tl = tiles[te.first + (int)(local % te.cnt)];
+        int mt, nt;
+        item_coords(w, NT, tiles, mt, nt);
+        const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
         const bool rows_here = rows > row0;

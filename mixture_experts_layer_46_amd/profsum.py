@@ -3,6 +3,8 @@
     python -m mixture_experts_layer_46_amd.profsum stats  <kernel_stats.csv> <out.txt> --command CMD
     python -m mixture_experts_layer_46_amd.profsum traffic <fetch_counter_collection.csv>
         <write_counter_collection.csv> <out.txt> --workload NAME --command CMD
+    python -m mixture_experts_layer_46_amd.profsum mfma <counter_collection.csv>
+        <kernel_trace.csv> <agent_info.csv> <out.txt> --workload NAME --command CMD
 
 `stats` tabulates calls and mean/min/max duration of each moe:: kernel from a
 `--kernel-trace --stats` run.  `traffic` averages FETCH_SIZE and WRITE_SIZE (KiB per
@@ -10,7 +12,10 @@ dispatch) of each moe:: kernel and scales them to HBM bytes with the factor the 
 counters give for the largest device copy in the run (a 1 GiB copy that the benchmark
 makes with --copy-calibration: true bytes / counted bytes).  The traffic file also
 records the sha256 of the grouped-GEMM source it was measured on, so a reader can tell
-when the kernel has changed since.
+when the kernel has changed since.  `mfma` takes one pass of SQ_VALU_MFMA_BUSY_CYCLES and
+GRBM_GUI_ACTIVE collected together with a kernel trace and reports, per kernel, the MFMA
+pipes' busy fraction (busy cycles summed over all SIMDs / (SIMDs x GPU cycles)) and the
+clock the kernel ran at (GUI-active cycles per XCC / duration).
 """
 from __future__ import annotations
 
@@ -118,6 +123,55 @@ def traffic(fetch_csv: str, write_csv: str, out_path: str, workload: str, comman
     return text
 
 
+def _gpu_agent(agent_csv: str):
+    for r in csv.DictReader(open(agent_csv)):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Simd_Count"]), int(r["Num_Xcc"]), int(r["Cu_Count"])
+    raise ValueError(f"no GPU agent in {agent_csv}")
+
+
+def mfma(counter_csv: str, trace_csv: str, agent_csv: str, out_path: str, workload: str, command: str) -> str:
+    simds, xccs, cus = _gpu_agent(agent_csv)
+    dur = {}
+    for r in csv.DictReader(open(trace_csv)):
+        dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    seen = collections.defaultdict(set)
+    for r in csv.DictReader(open(counter_csv)):
+        if not _is_moe(r["Kernel_Name"]):
+            continue
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        seen[short_name(r["Kernel_Name"])].add(r["Dispatch_Id"])
+    digest = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    lines = ["# rocprofv3 MFMA-busy summary (MoE kernels): SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs)",
+             "# and GRBM_GUI_ACTIVE (summed over XCCs) per dispatch, with durations from the same run",
+             f"# command: {command}",
+             f"# summary: python3 -m mixture_experts_layer_46_amd.profsum mfma {counter_csv} {trace_csv} "
+             f"{agent_csv} {out_path}",
+             f"workload: {workload}",
+             f"grouped_gemm.hip sha256: {digest}",
+             f"gpu: {cus} CUs, {simds} SIMDs, {xccs} XCCs",
+             "# clock and busy fraction only for kernels of at least 100 us", "",
+             f"{'dispatches':>10} {'mean_us':>9} {'clock_GHz':>9} {'mfma_busy':>9}  kernel"]
+    for name in sorted(seen):
+        ids = [i for i in seen[name] if i in dur and "GRBM_GUI_ACTIVE" in per[i]
+               and "SQ_VALU_MFMA_BUSY_CYCLES" in per[i]]
+        if not ids:
+            continue
+        us = sum(dur[i] for i in ids) / len(ids) / 1e3
+        gui = sum(per[i]["GRBM_GUI_ACTIVE"] for i in ids) / len(ids) / xccs
+        busy = sum(per[i]["SQ_VALU_MFMA_BUSY_CYCLES"] for i in ids) / len(ids) / simds
+        if us < 100:        # the counters' active window is not the kernel's: no rates
+            lines.append(f"{len(ids):10d} {us:9.1f} {'-':>9} {'-':>9}  {name}")
+            continue
+        clock = gui / (us * 1e3)
+        frac = busy / gui if gui > 0 else 0.0
+        lines.append(f"{len(ids):10d} {us:9.1f} {clock:9.2f} {frac:9.3f}  {name}")
+    text = "\n".join(lines) + "\n"
+    open(out_path, "w").write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -133,9 +187,18 @@ def main():
     b.add_argument("--command", required=True)
     b.add_argument("--up", default=None, help="name prefix of the first-projection kernel")
     b.add_argument("--down", default=None, help="name prefix of the second-projection kernel")
+    c = sub.add_parser("mfma")
+    c.add_argument("counter_csv")
+    c.add_argument("trace_csv")
+    c.add_argument("agent_csv")
+    c.add_argument("out")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats(args.csv, args.out, args.command), end="")
+    elif args.cmd == "mfma":
+        print(mfma(args.counter_csv, args.trace_csv, args.agent_csv, args.out, args.workload, args.command), end="")
     else:
         print(traffic(args.fetch_csv, args.write_csv, args.out, args.workload, args.command,
                       args.up, args.down), end="")
