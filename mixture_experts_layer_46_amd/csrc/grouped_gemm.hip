@@ -302,6 +302,21 @@ __device__ __forceinline__ void acc_zero(f32x4_t& a) {
 }
 
 __device__ __forceinline__ int fk(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+// 320-row tiles keep W rows of 384 bytes (SiLU2) or 192 bytes per matrix (SwiGLU): the
+// 32-byte block b of row k sits at b ^ fk320(k), within groups of 4 (384-byte rows) or
+// pairs (192-byte rows).  The rows one ds_read_b64_tr_b16 serves per LDS cycle (k0..k0+3
+// and k0+8..k0+11) then land on 8 distinct 32-byte bank slots (row starts are 128 or 64
+// bytes apart modulo 256).
+template <int NMAT>
+__device__ __forceinline__ int fk320(int k) {
+    return NMAT == 1 ? (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) : ((k >> 3) & 1);
+}
+// the LDS 32-byte block of logical W column block blk for a lane whose rows have swizzle g
+template <int BM, int NMAT>
+__device__ __forceinline__ int wblk(int blk, int g) {
+    if constexpr (BM == 320) return NMAT == 1 ? ((blk & ~3) | ((blk & 3) ^ g)) : ((blk & ~1) | ((blk & 1) ^ g));
+    else return (blk & ~7) | ((blk & 7) ^ g);
+}
 // A-row swizzle: 16-byte chunk q of tile row m sits at slot q ^ swa4(m).  On gfx950 a
 // ds_read_b128 serves 16 lanes per LDS cycle (64 banks), grouped by bit2^bit3^bit4 of
 // the lane index (lanes 0-3, 12-15 and 20-27 share a cycle; measured with the bank-
@@ -323,13 +338,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <int BM, int NMAT>
 struct LdsShape {
     static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, WAVES_M = 2, WAVES_N = 2, BK = 32;
-    static constexpr int NSTAGE = 4, LBN = 256, LBNm = LBN / NMAT;
+    // 320-row tiles keep W rows 192 wide in LDS (the columns they use), which makes room
+    // for a fifth stage: 5 x 32 KB = 160 KB
+    static constexpr int NSTAGE = BM == 320 ? 5 : 4, LBN = BM == 320 ? 192 : 256, LBNm = LBN / NMAT;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
     static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2, STAGE = A_STAGE + B_STAGE;
     static constexpr int ADMA = A_STAGE / 1024 / 4;   // A DMA instructions per wavefront per step
     static constexpr int BDMA = B_STAGE / 1024 / 4;   // W DMA instructions per wavefront per step
     static constexpr int DPW = ADMA + BDMA;
     static constexpr int BROW = 2 * LBNm;             // LDS bytes per W row
+    static constexpr int BMAT_DMA = B_STAGE / 1024 / NMAT;   // W DMA instructions per matrix
     static constexpr int CS_STRIDE = BNm + 8;
     static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
                                             ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
@@ -362,8 +380,9 @@ __device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t r
         // rows k0 >= K fall past the resource's K * rowB bytes and read zeros (the host
         // keeps (K + 128) * rowB below 2^32, so the offset cannot wrap)
         const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && j >= 8) ? rb1 : rb0,
-                                                 (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
+        constexpr int per_mat = S::BMAT_DMA;   // instructions of the first matrix
+        const __amdgpu_buffer_rsrc_t rb = (NMAT == 2 && j >= per_mat) ? rb1 : rb0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
     }
 }
 
@@ -407,7 +426,7 @@ __device__ __attribute__((always_inline)) inline void kstep(
             mat = fn < FN / 2 ? 0 : 1;
             blk = wn * (FN / 2) + (fn % (FN / 2));
         }
-        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (((blk & ~7) | ((blk & 7) ^ g)) << 5);
+        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (wblk<BM, NMAT>(blk, g) << 5);
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
         const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -507,7 +526,8 @@ __device__ __attribute__((always_inline)) inline void rows_item(
 // Wait until at most `pending` K steps' DMA of this wavefront are still in flight.
 template <int DPW>
 __device__ __forceinline__ void wait_dma(int pending) {
-    if (pending >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");
+    if (pending >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * DPW) : "memory");
+    else if (pending == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DPW) : "memory");
     else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -544,7 +564,8 @@ __device__ __forceinline__ void gemm_tiles(
 
     // fragment read offsets: A row (wm*WTM + 16 fm + l16) chunk lq; W rows 8 lq + (l16 >> 2)
     const int a_rd = (wm * WTM + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
-    const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);             // fk(k) / 2 of this lane's rows
+    // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
+    const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
 
     for (long long w = first; w < total; w += G) {
@@ -581,12 +602,17 @@ __device__ __forceinline__ void gemm_tiles(
         const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + eoff, (uint32_t)K * rowB);
         const __amdgpu_buffer_rsrc_t rb1 = make_rsrc((NMAT == 2 ? B1 : B0) + eoff, (uint32_t)K * rowB);
         // W: instruction j covers 2 rows x 32 chunks (SiLU2 / second projection) or
-        // 4 rows x 16 chunks of one matrix (SwiGLU)
+        // 4 rows x 16 chunks of one matrix (SwiGLU); for 320-row tiles, LDS bytes
+        // [1024 j, 1024 j + 1024) of rows 384 (SiLU2) or 192 (SwiGLU, per matrix) bytes wide
 #pragma unroll
         for (int i = 0; i < BDMA; ++i) {
             const int j = wave * BDMA + i;
             int k, c;
-            if constexpr (NMAT == 1) {
+            if constexpr (BM == 320) {
+                const int pos = (j % S::BMAT_DMA) * 1024 + lane * 16;   // byte within the matrix
+                k = pos / BROW;
+                c = ((pos % BROW) / 16) ^ (2 * fk320<NMAT>(k));
+            } else if constexpr (NMAT == 1) {
                 k = j * 2 + (lane >> 5);
                 c = (lane & 31) ^ fk(k);
             } else {
@@ -790,7 +816,7 @@ __device__ __forceinline__ void pp_read(const lds_char* st, int a_rd, int b_rd, 
             mat = fn < FN / 2 ? 0 : 1;
             blk = wn * (FN / 2) + (fn % (FN / 2));
         }
-        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (((blk & ~7) | ((blk & 7) ^ g)) << 5);
+        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (wblk<BM, NMAT>(blk, g) << 5);
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
         const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
