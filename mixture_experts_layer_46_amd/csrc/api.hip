@@ -42,11 +42,21 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout shared by every entry point (offsets from the workspace base).
 struct Layout {
     size_t logits, topk_idx, topk_w, counts, offsets, segcnt, sorted_token, row_of_pair,
-        tiles, ntiles, h, y, total;
+        tiles, ntiles, part_cnt, parts, h, y, total;
 };
 
 long long max_tiles_for(long long P, int E, int BM) {
     return (P + BM - 1) / BM + (P < E ? P : E);
+}
+
+// Row-tile height of the grouped GEMM from the mean rows per expert (host only knows
+// T*k/E; per-expert counts stay on the device).
+GemmCfg pick_cfg(const moe_shape& s) {
+    const double mean = (double)s.T * s.k / s.E;
+    if (mean <= 24) return GEMM_M16;
+    if (mean <= 80) return GEMM_M64;
+    if (mean <= 160) return GEMM_M128;
+    return GEMM_M256;                    // 256 or 320 rows, chosen on the device
 }
 
 Layout layout_of(const moe_shape& s) {
@@ -65,6 +75,10 @@ Layout layout_of(const moe_shape& s) {
     L.row_of_pair = o;  o += up(P * 4);
     L.tiles = o;        o += up((size_t)max_tiles_for((long long)P, s.E, 16) * sizeof(Tile));
     L.ntiles = o;       o += up(4);
+    // the bf16 grouped GEMM's split of the last round: part slots and their counters
+    const bool split = s.dtype == MOE_BF16 && pick_cfg(s) != GEMM_M16;
+    L.part_cnt = o;     o += split ? up((size_t)kGemmPartSlots * 4) : 0;
+    L.parts = o;        o += split ? up((size_t)kGemmPartSlots * kGemmPartSlotFloats * 4) : 0;
     L.h = o;            o += up(P * s.F * es);
     L.y = o;            o += up(P * s.H * es);
     L.total = o;
@@ -125,15 +139,6 @@ moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes) {
     return MOE_OK;
 }
 
-// Row-tile height of the grouped GEMM from the mean rows per expert (host only knows
-// T*k/E; per-expert counts stay on the device).
-GemmCfg pick_cfg(const moe_shape& s) {
-    const double mean = (double)s.T * s.k / s.E;
-    if (mean <= 24) return GEMM_M16;
-    if (mean <= 80) return GEMM_M64;
-    if (mean <= 160) return GEMM_M128;
-    return GEMM_M256;                    // 256 or 320 rows, chosen on the device
-}
 
 moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_rows,
                        const int32_t* offsets, const void* w_in, const void* w_up,
@@ -146,7 +151,7 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     int32_t* ntiles = at<int32_t>(ws, L.ntiles);
     if (s.dtype == MOE_F32) {
         const int BM = 64;
-        HIPCHK(launch_build_tiles(offsets, s.E, BM, BM, 1, 1, tiles, ntiles, st), "build_tiles");
+        HIPCHK(launch_build_tiles(offsets, s.E, BM, BM, 1, 1, tiles, ntiles, nullptr, st), "build_tiles");
         HIPCHK(launch_grouped_ffn_f32(a, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
                                       ntiles, max_tiles_for(P, s.E, BM), s.H, s.F, swiglu, ev, st),
                "grouped_ffn_f32");
@@ -155,9 +160,11 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     const GemmCfg cfg = pick_cfg(s);
     int bma, bmb;
     gemm_cfg_heights(cfg, &bma, &bmb);
-    HIPCHK(launch_build_tiles_for(offsets, s.E, cfg, s.H, s.F, swiglu, tiles, ntiles, st), "build_tiles");
+    SplitBuffers sb{nullptr, nullptr};
+    if (cfg != GEMM_M16) sb = SplitBuffers{at<float>(ws, L.parts), at<int>(ws, L.part_cnt)};
+    HIPCHK(launch_build_tiles_for(offsets, s.E, cfg, s.H, s.F, swiglu, tiles, ntiles, sb.counts, st), "build_tiles");
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
-                                   ntiles, max_tiles_for(P, s.E, std::min(bma, bmb)), cfg, s.H, s.F, swiglu, ev, st),
+                                   ntiles, max_tiles_for(P, s.E, std::min(bma, bmb)), cfg, s.H, s.F, swiglu, sb, ev, st),
            "grouped_ffn_bf16");
     return MOE_OK;
 }

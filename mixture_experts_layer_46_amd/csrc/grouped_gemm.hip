@@ -458,19 +458,20 @@ template <int DPW>
 __device__ __forceinline__ void wait_dma(int pending);
 __device__ __forceinline__ void kloop_barrier();
 
-// The K loop of one work item for a wavefront whose rows fill FMA 16-row blocks.
+// The K loop of one work item for a wavefront whose rows fill FMA 16-row blocks: KT
+// steps starting at step kt0 (the DMA of steps kt0 .. kt0 + NSTAGE - 2 is in flight).
 template <int BM, int NMAT, int FMA>
 __device__ __attribute__((always_inline)) inline void kloop(
     lds_char* lds, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K, uint32_t rowB, int wave,
-    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN]) {
+    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN], int kt0) {
     using S = LdsShape<BM, NMAT>;
     constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE;
     for (int kt = 0; kt < KT; ++kt) {
         wait_dma<S::DPW>(NSTAGE - 2);
         kloop_barrier();
         kstep<BM, NMAT, FMA>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
-                             ra, rb0, rb1, pl, kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+                             ra, rb0, rb1, pl, kt0 + kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
     }
 }
 
@@ -482,6 +483,88 @@ __device__ __attribute__((always_inline)) inline void kloop(
 // memory clobber still keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Split of the last round's items along K.  A persistent launch of G workgroups runs its
+// items in rounds of G; when the last round is partial, its items are split along K into
+// `split` parts, so that round is filled with shorter work.  Each part writes its fp32
+// accumulators (in register layout) to a slot of the part buffer; the last part of an item
+// to finish (counted with one atomic per item) adds all parts in part order, so the sum
+// does not depend on which part finished last, and writes the output as an unsplit item
+// would.  Nothing waits for another workgroup.
+constexpr int kPartSlots = kGemmPartSlots;   // parts in flight at most (slots of the part buffer)
+constexpr int kMaxSplit = 8;
+constexpr int kMinPartSteps = 32;     // K steps per part at least (1024 of K)
+
+struct SplitPart {
+    float* buf;       // this part's slot; NULL when the item is not split
+    float* item;      // the item's first slot (its `split` slots are consecutive)
+    int* cnt;         // the item's arrival counter
+    int split;
+    size_t slot_floats;
+};
+
+// Decides the split of a launch and maps work index w to (item, part).
+struct WorkSplit {
+    long long full, nwork;
+    int rem, split;
+    __device__ WorkSplit(long long total, int G, int KT) {
+        full = total / G * G;
+        rem = (int)(total - full);
+        split = 1;
+        if (rem > 0 && KT >= 2 * kMinPartSteps) {
+            const int by_slots = (G < kPartSlots ? G : kPartSlots) / rem;
+            const int by_steps = KT / kMinPartSteps;
+            split = min(min(by_slots, by_steps), kMaxSplit);
+            if (split < 1) split = 1;
+        }
+        nwork = full + (long long)rem * split;
+    }
+    __device__ void item_of(long long w, long long& item, int& part, int& slot) const {
+        if (split == 1 || w < full) {
+            item = w;
+            part = 0;
+            slot = -1;
+        } else {
+            const int p = (int)(w - full);
+            slot = p % rem;
+            part = p / rem;
+            item = full + slot;
+        }
+    }
+};
+
+// Parts travel through device-scope (sc1) buffer stores and loads: such accesses are
+// coherent across the XCDs' L2 caches on their own, so the hand-off needs no L2-wide
+// write-back or invalidate (which would also evict the tiles other workgroups on the
+// XCD are reusing), only that this workgroup's part stores have completed before its
+// arrival is counted.
+constexpr int kDeviceScope = 16;      // the sc1 bit of a buffer access's cache policy
+
+__device__ __forceinline__ void store_part(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, kDeviceScope);
+}
+
+__device__ __forceinline__ f32x4_t load_part(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceScope));
+}
+
+// Arrival of a workgroup that has written its part: returns (uniformly) whether it is the
+// item's last part.  Every wavefront waits for its part stores to complete before the
+// barrier that precedes the count, so when the count reaches `split` all parts are in
+// place for the last arriver's device-scope loads.  `flag` is an LDS word outside the
+// staging tile.  The last arriver re-zeroes the counter for the next launch.
+__device__ __forceinline__ bool split_arrive(const SplitPart& sp, int* flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = atomicAdd(sp.cnt, 1);
+        const int last = old == sp.split - 1;
+        if (last) atomicExch(sp.cnt, 0);
+        *flag = last;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
 // The rows part of one work item for a wavefront whose rows fill FMA 16-row blocks: the
 // K loop into accumulators of exactly those blocks, then (after the workgroup barrier
 // that frees the LDS stages) the activation and the bf16 rounding of its rows into the
@@ -489,10 +572,11 @@ __device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "
 // never sees accumulators of one variant live in another.  Barriers: KT + 1, as in the
 // DMA-only path of a wavefront without rows.
 template <int BM, int NMAT, int ACT, int FMA>
-__device__ __attribute__((always_inline)) inline void rows_item(
-    lds_char* lds, bf16_t* sC, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+__device__ __attribute__((always_inline)) inline bool rows_item(
+    lds_char* lds, bf16_t* sC, int kt0, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
     __amdgpu_buffer_rsrc_t rb1, const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K,
-    uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn, int rb, int wrows, int lq, int l16) {
+    uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn, int rb, int wrows, int lq, int l16,
+    const SplitPart& sp, int* flag) {
     using S = LdsShape<BM, NMAT>;
     constexpr int FN = S::FN, FO = (NMAT == 2) ? FN / 2 : FN, BNm = S::BNm, WTN = S::WTN;
     f32x4_t acc[FMA][FN];
@@ -500,9 +584,39 @@ __device__ __attribute__((always_inline)) inline void rows_item(
     for (int i = 0; i < FMA; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc_zero(acc[i][j]);
-    kloop<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+    kloop<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc, kt0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
     __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const size_t wofs = (size_t)wave * S::FM * FN * 256 + lane * 4;
+    // the item's part slots, and this part's byte offset within them (wavefront-uniform;
+    // taken through readfirstlane so that the compiler keeps the descriptor in SGPRs)
+    const uint64_t ib = (uint64_t)(uintptr_t)sp.item;
+    const uint32_t ib_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ib);
+    const uint32_t ib_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ib >> 32));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+        (const void*)(uintptr_t)(((uint64_t)ib_hi << 32) | ib_lo),
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(sp.split * sp.slot_floats * 4)));
+    const uint32_t pofs = (uint32_t)__builtin_amdgcn_readfirstlane((int)((sp.buf - sp.item) * 4));
+    if (sp.buf) {
+        // one part of a split item: store the accumulators (register layout, 16 bytes per
+        // lane per block); the item's last part then reads all parts back in part order
+        // (below), so its accumulators are not needed past this point
+#pragma unroll
+        for (int fm = 0; fm < FMA; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                store_part(rp, pofs + (uint32_t)((wofs + (size_t)(fm * FN + fn) * 256) * 4), acc[fm][fn]);
+        if (!split_arrive(sp, flag)) return false;
+    }
+    // block (fm, fn) of the finished sums: the accumulators, or the parts added in order
+    auto block = [&](int fm, int fn) -> f32x4_t {
+        if (!sp.buf) return acc[fm][fn];
+        const uint32_t o = (uint32_t)((wofs + (size_t)(fm * FN + fn) * 256) * 4);
+        f32x4_t sum = load_part(rp, o);
+        for (int q = 1; q < sp.split; ++q) sum += load_part(rp, o + (uint32_t)(q * sp.slot_floats * 4));
+        return sum;
+    };
 #pragma unroll
     for (int fm = 0; fm < FMA; ++fm) {
         // only this wavefront's row blocks (with the even split of a 320-row tile, the
@@ -511,16 +625,20 @@ __device__ __attribute__((always_inline)) inline void rows_item(
 #pragma unroll
         for (int fo = 0; fo < FO; ++fo) {
             const int col = (NMAT == 2 ? wn * (BNm / S::WAVES_N) : wn * WTN) + 16 * fo + l16;
+            const f32x4_t x = block(fm, fo);
+            f32x4_t u = x;
+            if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                float val = acc[fm][fo][v];
-                if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
+                float val = x[v];
+                if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
                 else if constexpr (ACT == 1) val = silu_f32(val);
                 const int r = rb + 16 * fm + 4 * lq + v;
                 sC[r * S::CS_STRIDE + col] = f32_to_bf16(val);
             }
         }
     }
+    return true;
 }
 
 // Wait until at most `pending` K steps' DMA of this wavefront are still in flight.
@@ -533,12 +651,17 @@ __device__ __forceinline__ void wait_dma(int pending) {
 }
 
 // All work items of one launch for row tiles of height BM (the persistent loop).
+// part_buf / part_cnt: kPartSlots slots of BM x BN floats and kPartSlots counters (zero
+// on entry) for the split of the last round, or NULL (no split).  Only the second
+// projection splits: its K (the FFN width) is long, so a part's fp32 slot is small beside
+// its operand stream; on the first projection (K = the model width) a split measured no
+// faster, and the split's code alone made that kernel slower, so it is compiled out there.
 template <int BM, int NMAT, int ACT, bool GATHER>
 __device__ __forceinline__ void gemm_tiles(
     uint4* smem, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     using S = LdsShape<BM, NMAT>;
     constexpr int BNm = S::BNm, WAVES_N = S::WAVES_N, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
     constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, ADMA = S::ADMA, BDMA = S::BDMA;
@@ -548,6 +671,12 @@ __device__ __forceinline__ void gemm_tiles(
 
     lds_char* lds = (lds_char*)smem;
     bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
+    // the split parts' arrival flag: an LDS word past the output staging tile
+    constexpr int FLAG_OFF = (BM * CS_STRIDE * 2 + 15) / 16 * 16;
+    static_assert(FLAG_OFF + 16 <= (int)S::LDS_BYTES, "no LDS word left for the arrival flag");
+    int* flag = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + FLAG_OFF);
+    constexpr size_t SLOT = (size_t)BM * S::BN;       // floats per part slot
+    static_assert(SLOT <= kGemmPartSlotFloats, "part slot larger than the workspace's");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -568,13 +697,34 @@ __device__ __forceinline__ void gemm_tiles(
     const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
 
-    for (long long w = first; w < total; w += G) {
-        // decode the work item (order: item_coords)
+    float* const pbuf = GATHER ? nullptr : part_buf;
+    const WorkSplit wsp(total, G, pbuf ? KT : 0);
+    for (long long w = first; w < wsp.nwork; w += G) {
+        // decode the work item (order: item_coords) and, for a split item, its part
+        long long item;
+        int part, slot;
+        wsp.item_of(w, item, part, slot);
+        // the item is the same for the whole workgroup: keep it (and what derives from it,
+        // the tile, the operand resources) in scalar registers
+        part = __builtin_amdgcn_readfirstlane(part);
+        slot = __builtin_amdgcn_readfirstlane(slot);
         int mt, nt;
-        item_coords(w, NT, tiles, mt, nt);
+        item_coords(item, NT, tiles, mt, nt);
+        mt = __builtin_amdgcn_readfirstlane(mt);
+        nt = __builtin_amdgcn_readfirstlane(nt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
+        // K range of this work: all of K for an item of a complete round, else its part
+        const int parts = slot >= 0 ? wsp.split : 1;
+        const int kt0 = __builtin_amdgcn_readfirstlane((int)((long long)part * KT / parts));
+        const int nsteps = __builtin_amdgcn_readfirstlane((int)((long long)(part + 1) * KT / parts) - kt0);
+        SplitPart sp{nullptr, nullptr, nullptr, wsp.split, SLOT};
+        if (pbuf && slot >= 0) {
+            sp.item = pbuf + (size_t)slot * wsp.split * SLOT;
+            sp.buf = sp.item + (size_t)part * SLOT;
+            sp.cnt = part_cnt + slot;
+        }
         // 320-row tiles split the tile's rows evenly between the two wavefront rows (at a
         // multiple of 16, so the A swizzle is unchanged): an expert with 256 rows then
         // multiplies 8 row blocks per wavefront instead of 10 and 6
@@ -624,36 +774,38 @@ __device__ __forceinline__ void gemm_tiles(
             pl.b_off[i] = (8 * c < BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
         }
 
-        // prologue: steps 0..NSTAGE-2 in flight (steps past K read zeros, see kstep)
+        // prologue: steps kt0..kt0+NSTAGE-2 in flight (steps past K read zeros, see kstep)
 #pragma unroll
         for (int t = 0; t < NSTAGE - 1; ++t)
-            dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
+            dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, kt0 + t, K, rowB, wave);
+        bool write_out;       // the same in every wavefront of the workgroup
         if (wave_rows) {
             // a wavefront whose rows fill only the first blocks of its tile multiplies just
             // those (1, 2, 4, and for 320-row tiles 8 or 9 blocks of 16 rows, else all)
             const int ar = a_rd_item;
-#define MOE_ROWS_ITEM(F_) rows_item<BM, NMAT, ACT, (F_)>(lds, sC, KT, ra, rb0, rb1, pl, K, rowB, wave, ar, \
-                                                           b_rd, g, wn, rb, wrows, lq, l16)
-            if (wrows <= 16) MOE_ROWS_ITEM(1);
-            else if (FM > 2 && wrows <= 32) MOE_ROWS_ITEM(FM > 2 ? 2 : FM);
-            else if (FM > 4 && wrows <= 64) MOE_ROWS_ITEM(FM > 4 ? 4 : FM);
-            else if (BM == 320 && wrows <= 128) MOE_ROWS_ITEM(BM == 320 ? 8 : FM);
-            else if (BM == 320 && wrows <= 144) MOE_ROWS_ITEM(BM == 320 ? 9 : FM);
-            else MOE_ROWS_ITEM(FM);
+#define MOE_ROWS_ITEM(F_) rows_item<BM, NMAT, ACT, (F_)>(lds, sC, kt0, nsteps, ra, rb0, rb1, pl, K, rowB, wave, \
+                                                           ar, b_rd, g, wn, rb, wrows, lq, l16, sp, flag)
+            if (wrows <= 16) write_out = MOE_ROWS_ITEM(1);
+            else if (FM > 2 && wrows <= 32) write_out = MOE_ROWS_ITEM(FM > 2 ? 2 : FM);
+            else if (FM > 4 && wrows <= 64) write_out = MOE_ROWS_ITEM(FM > 4 ? 4 : FM);
+            else if (BM == 320 && wrows <= 128) write_out = MOE_ROWS_ITEM(BM == 320 ? 8 : FM);
+            else if (BM == 320 && wrows <= 144) write_out = MOE_ROWS_ITEM(BM == 320 ? 9 : FM);
+            else write_out = MOE_ROWS_ITEM(FM);
 #undef MOE_ROWS_ITEM
         } else {       // no rows for this wavefront: it still moves its share of the tiles
-            for (int kt = 0; kt < KT; ++kt) {
+            for (int kt = 0; kt < nsteps; ++kt) {
                 wait_dma<S::DPW>(NSTAGE - 2);
                 kloop_barrier();
                 dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
-                                   kt + NSTAGE - 1, K, rowB, wave);
+                                   kt0 + kt + NSTAGE - 1, K, rowB, wave);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            write_out = sp.buf ? split_arrive(sp, flag) : true;
         }
         __syncthreads();
         constexpr int CPR = BNm / 8;
-        for (int c = tid; c < rows * CPR; c += 256) {
+        for (int c = tid; write_out && c < rows * CPR; c += 256) {
             const int r = c / CPR, cc = c % CPR;
             const int col = n0 + cc * 8;
             if (col < N)
@@ -683,14 +835,16 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     extern __shared__ uint4 smem[];
     const int bm = __builtin_amdgcn_readfirstlane(ntiles_p[1]);
     if (BMA == BMB && bm != BMA) return;      // the list is for the other kernel of the launch pair
     if (BMA != BMB && bm == BMB)
-        gemm_tiles<BMB, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+        gemm_tiles<BMB, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
+                                           part_buf, part_cnt);
     else
-        gemm_tiles<BMA, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+        gemm_tiles<BMA, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
+                                           part_buf, part_cnt);
 }
 
 // ------------------------------------------- ping-pong variant (two wavefront groups)
@@ -1006,7 +1160,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_pp(
 __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__ offsets, int E,
                                                      int BMA, int BMB, int wa, int wb,
                                                      Tile* __restrict__ tiles,
-                                                     int32_t* __restrict__ ntiles) {
+                                                     int32_t* __restrict__ ntiles, int* __restrict__ part_cnt) {
+    // the grouped GEMMs' split-part counters start at zero (each launch leaves them so)
+    static_assert(kPartSlots <= 256, "one counter per thread");
+    if (part_cnt && threadIdx.x < kPartSlots) part_cnt[threadIdx.x] = 0;
     __shared__ int buf[2][256];
     __shared__ long long cost[2][4];
     const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
@@ -1050,8 +1207,9 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int BMA, int BMB, int wa, int wb,
-                              Tile* tiles, int32_t* ntiles, hipStream_t st) {
-    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(256), 0, st, offsets, E, BMA, BMB, wa, wb, tiles, ntiles);
+                              Tile* tiles, int32_t* ntiles, int* part_cnt, hipStream_t st) {
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(256), 0, st, offsets, E, BMA, BMB, wa, wb, tiles, ntiles,
+                       part_cnt);
     return hipGetLastError();
 }
 
@@ -1081,11 +1239,11 @@ static int col_blocks(int BM, int H, int F, int swiglu) {
 }
 
 hipError_t launch_build_tiles_for(const int32_t* offsets, int E, GemmCfg cfg, int H, int F, int swiglu,
-                                  Tile* tiles, int32_t* ntiles, hipStream_t st) {
+                                  Tile* tiles, int32_t* ntiles, int* part_cnt, hipStream_t st) {
     int a, b;
     gemm_cfg_heights(cfg, &a, &b);
     return launch_build_tiles(offsets, E, a, b, col_blocks(a, H, F, swiglu), col_blocks(b, H, F, swiglu),
-                              tiles, ntiles, st);
+                              tiles, ntiles, part_cnt, st);
 }
 
 // ------------------------------------------------------------------------ launching
@@ -1116,7 +1274,7 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
 template <int BM, int BMB, int NMAT, int WAVES_M, int ACT, bool GATHER>
 static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
                            const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
-                           long long max_items, int K, int N, hipStream_t st) {
+                           long long max_items, int K, int N, const SplitBuffers& sb, hipStream_t st) {
     static bool ready = false;
     static int occ = 1;
     unsigned G = 0;
@@ -1145,7 +1303,8 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
             e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
-                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
+                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows,
+                               sb.parts, sb.counts);
             return hipGetLastError();
         } else {
             constexpr size_t lds_bytes = LdsPair<BM, BMB>::template bytes<NMAT>();
@@ -1153,7 +1312,8 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
             hipError_t e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(kern, dim3(G), dim3(256), lds_bytes, st, (const bf16_t*)A, gather_rows,
-                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
+                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows,
+                               sb.parts, sb.counts);
         }
     }
     return hipGetLastError();
@@ -1163,22 +1323,22 @@ template <int BM, int BMB, int WAVES_M>
 static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather_rows, const void* w_in,
                           const void* w_up, const void* w_out, void* h, void* y,
                           const Tile* tiles, const int32_t* ntiles, long long max_tiles,
-                          int H, int F, int swiglu, const hipEvent_t* ev, hipStream_t st) {
+                          int H, int F, int swiglu, const SplitBuffers& sb, const hipEvent_t* ev, hipStream_t st) {
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
     // work items (row tiles x column blocks) bound the persistent grid: the larger of the
     // two shapes' counts (max_tiles is counted for the lower height)
     const long long items = max_tiles * std::max(col_blocks(BM, H, F, swiglu), col_blocks(BMB, H, F, swiglu));
     if (swiglu) {
-        e = gather_rows ? run_gemm<BM, BMB, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items, H, F, st)
-                        : run_gemm<BM, BMB, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items, H, F, st);
+        e = gather_rows ? run_gemm<BM, BMB, 2, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, w_up, h, tiles, ntiles, items, H, F, sb, st)
+                        : run_gemm<BM, BMB, 2, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, w_up, h, tiles, ntiles, items, H, F, sb, st);
     } else {
-        e = gather_rows ? run_gemm<BM, BMB, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items, H, F, st)
-                        : run_gemm<BM, BMB, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items, H, F, st);
+        e = gather_rows ? run_gemm<BM, BMB, 1, WAVES_M, 1, true>(a, a_rows, gather_rows, w_in, nullptr, h, tiles, ntiles, items, H, F, sb, st)
+                        : run_gemm<BM, BMB, 1, WAVES_M, 1, false>(a, a_rows, nullptr, w_in, nullptr, h, tiles, ntiles, items, H, F, sb, st);
     }
     if (e != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-    e = run_gemm<BM, BMB, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items, F, H, st);
+    e = run_gemm<BM, BMB, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items, F, H, sb, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     return e;
 }
@@ -1187,16 +1347,16 @@ hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   const hipEvent_t* ev, hipStream_t st) {
+                                   const SplitBuffers& sb, const hipEvent_t* ev, hipStream_t st) {
     switch (cfg) {
         case GEMM_M16:
-            return run_ffn<16, 16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<16, 16, 1>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, sb, ev, st);
         case GEMM_M64:
-            return run_ffn<64, 64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<64, 64, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, sb, ev, st);
         case GEMM_M128:
-            return run_ffn<128, 128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<128, 128, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, sb, ev, st);
         default:
-            return run_ffn<256, 320, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, ev, st);
+            return run_ffn<256, 320, 2>(a, a_rows, gather_rows, w_in, w_up, w_out, h, y, tiles, ntiles, max_tiles, H, F, swiglu, sb, ev, st);
     }
 }
 

@@ -23,6 +23,16 @@ struct Tile {
     int e, row0, row1, first, cnt, pad0, pad1, pad2;
 };
 
+// Workspace of the bf16 grouped GEMM's split of the last round (see grouped_gemm.hip):
+// kGemmPartSlots slots of up to kGemmPartSlotFloats fp32 accumulators, and as many int
+// counters (zeroed by the tile builder).  NULL buffers switch the split off.
+constexpr int kGemmPartSlots = 256;
+constexpr size_t kGemmPartSlotFloats = 256 * 256;    // the largest tile, BM x BN
+struct SplitBuffers {
+    float* parts;
+    int* counts;
+};
+
 // Tile configurations of the bf16 grouped GEMM.  GEMM_M256 lets the tile builder choose
 // 256- or 320-row tiles per launch from the actual per-expert counts.
 enum GemmCfg { GEMM_M16 = 0, GEMM_M64 = 1, GEMM_M128 = 2, GEMM_M256 = 3 };
@@ -47,10 +57,10 @@ hipError_t launch_gather(const void* x, const int32_t* sorted_token, const int32
 // tile list for heights BMA / BMB (the one with fewer work items; wa, wb = column blocks
 // per row tile); ntiles[0] = tile count, ntiles[1] = the height chosen
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int BMA, int BMB, int wa, int wb,
-                              Tile* tiles, int32_t* ntiles, hipStream_t st);
+                              Tile* tiles, int32_t* ntiles, int* part_cnt, hipStream_t st);
 // the same for a bf16 configuration of the grouped FFN
 hipError_t launch_build_tiles_for(const int32_t* offsets, int E, GemmCfg cfg, int H, int F, int swiglu,
-                                  Tile* tiles, int32_t* ntiles, hipStream_t st);
+                                  Tile* tiles, int32_t* ntiles, int* part_cnt, hipStream_t st);
 
 // grouped FFN.  A rows: x_perm rows directly (gather_rows == NULL) or x[gather_rows[r]]
 // with x holding a_rows rows (its bytes must stay below 2^32 for the 32-bit buffer
@@ -60,7 +70,7 @@ hipError_t launch_grouped_ffn_bf16(const void* a, long long a_rows, const int32_
                                    const void* w_in, const void* w_up, const void* w_out,
                                    void* h, void* y, const Tile* tiles, const int32_t* ntiles,
                                    long long max_tiles, GemmCfg cfg, int H, int F, int swiglu,
-                                   const hipEvent_t* ev, hipStream_t st);
+                                   const SplitBuffers& sb, const hipEvent_t* ev, hipStream_t st);
 hipError_t launch_grouped_ffn_f32(const void* a, const int32_t* gather_rows,
                                   const void* w_in, const void* w_up, const void* w_out,
                                   void* h, void* y, const Tile* tiles, const int32_t* ntiles,

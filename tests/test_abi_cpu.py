@@ -139,10 +139,15 @@ def test_status_strings(lib):
 
 
 def test_workspace_grows_with_the_layer(lib):
-    a = _ws(lib, _shape())
-    b = _ws(lib, _shape(T=1024))
+    a = _ws(lib, _shape())                              # 4 rows per expert: 16-row tiles
+    b = _ws(lib, _shape(T=1024))                        # 256 rows per expert: large tiles
     c = _ws(lib, _shape(T=1024, dtype=_lib.MOE_F32))
-    assert 0 < a < b < c
+    d = _ws(lib, _shape(dtype=_lib.MOE_F32))
+    assert 0 < a < b and 0 < d < c
+    # the large-tile bf16 GEMM carries the split buffers of its last round: 256 slots of
+    # up to 256 x 256 fp32 accumulators (the 16-row tiles and fp32 layers have none)
+    assert b - a > 256 * 256 * 256 * 4
+    assert c - d < 256 * 256 * 256 * 4
 
 
 def test_capacity_rows():
