@@ -34,6 +34,7 @@
 //   * The epilogue applies SiLU / SwiGLU in fp32, rounds to bf16 once, stages the tile
 //     in LDS and writes whole rows with 16-byte stores.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -492,7 +493,7 @@ __device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "
 // would.  Nothing waits for another workgroup.
 constexpr int kPartSlots = kGemmPartSlots;   // parts in flight at most (slots of the part buffer)
 constexpr int kMaxSplit = 8;
-constexpr int kMinPartSteps = 32;     // K steps per part at least (1024 of K)
+constexpr int kMinPartSteps = 64;     // K steps per part at least (2048 of K)
 
 struct SplitPart {
     float* buf;       // this part's slot; NULL when the item is not split
@@ -877,8 +878,10 @@ struct PpShape {
     static constexpr int BDMA = B_INSTR / 8;
     static constexpr int DPW0 = ADMA0 + BDMA, DPW1 = ADMA1 + BDMA;
     static constexpr int BROW = 2 * LBNm, CS_STRIDE = BNm + 8;
-    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
-                                            ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
+    // the split parts' arrival flag: an LDS word past the output staging tile
+    static constexpr int FLAG_OFF = (BM * CS_STRIDE * 2 + 15) / 16 * 16;
+    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)FLAG_OFF + 16
+                                            ? (size_t)NSTAGE * STAGE : (size_t)FLAG_OFF + 16;
     static_assert(A_INSTR % 8 == 0 || A_INSTR % 8 == 4, "A instructions split by groups");
     static_assert(B_INSTR % 8 == 0, "W instructions split evenly");
 };
@@ -945,7 +948,7 @@ __device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& p
 // The whole K loop of one work item for group GROUP: plan, prologue, loop.
 template <int GROUP, int BM, int NMAT, bool GATHER>
 __device__ __attribute__((always_inline)) inline void pp_item(
-    lds_char* lds, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
+    lds_char* lds, int kt0, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]);
@@ -978,11 +981,12 @@ __device__ __forceinline__ void pp_read(const lds_char* st, int a_rd, int b_rd, 
     }
 }
 
-// The K loop of one group (see the phase table above).  `rows_here`: the wavefront has
-// rows of the tile (else it only moves its DMA share and keeps the barriers).
+// The K loop of one group (see the phase table above) over K steps kt0 .. kt0 + KT - 1.
+// `rows_here`: the wavefront has rows of the tile (else it only moves its DMA share and
+// keeps the barriers).
 template <int GROUP, int BM, int NMAT>
 __device__ __attribute__((always_inline)) inline void pp_kloop(
-    lds_char* lds, int KT, bool rows_here, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+    lds_char* lds, int kt0, int KT, bool rows_here, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
     __amdgpu_buffer_rsrc_t rb1,
     const PpPlan<GROUP == 0 ? PpShape<BM, NMAT>::ADMA0 : PpShape<BM, NMAT>::ADMA1, PpShape<BM, NMAT>::BDMA>& pl,
     int K, uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn,
@@ -995,8 +999,8 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
     if constexpr (GROUP == 1) kloop_barrier();                  // group 1's idle first phase
     for (int kt = 0; kt < KT; ++kt) {
         // read phase: DMA of stage kt + 3 into the slot of stage kt - 1, fragments of stage kt
-        pp_dma<BM, NMAT, ADMA>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl, kt + NSTAGE - 1, K,
-                               rowB, wave);
+        pp_dma<BM, NMAT, ADMA>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl, kt0 + kt + NSTAGE - 1,
+                               K, rowB, wave);
         if (rows_here) pp_read<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, a_rd, b_rd, g, wn, af, bfr);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (GROUP == 1) wait_dma<DPW>(2);              // stage kt + 1 complete
@@ -1023,7 +1027,7 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
 
 template <int GROUP, int BM, int NMAT, bool GATHER>
 __device__ __attribute__((always_inline)) inline void pp_item(
-    lds_char* lds, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
+    lds_char* lds, int kt0, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
@@ -1035,25 +1039,31 @@ __device__ __attribute__((always_inline)) inline void pp_item(
     // prologue: stages 0..2 in flight, stage 0 complete for all before the first reads
 #pragma unroll
     for (int t = 0; t < S::NSTAGE - 1; ++t)
-        pp_dma<BM, NMAT, ADMA>(lds + t * S::STAGE, ra, rb0, rb1, pl, t, K, rowB, wave);
+        pp_dma<BM, NMAT, ADMA>(lds + t * S::STAGE, ra, rb0, rb1, pl, kt0 + t, K, rowB, wave);
     wait_dma<ADMA + S::BDMA>(2);
     kloop_barrier();
-    pp_kloop<GROUP, BM, NMAT>(lds, KT, rows_here, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+    pp_kloop<GROUP, BM, NMAT>(lds, kt0, KT, rows_here, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
 }
 
-template <int BM, int NMAT, int ACT, bool GATHER>
+// All work items of one launch, ping-pong form.  part_buf / part_cnt as for gemm_tiles
+// (the split of the last round), used by the SPLIT instance only.
+template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
 __device__ __forceinline__ void gemm_tiles_pp(
     uint4* smem, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     using S = PpShape<BM, NMAT>;
     constexpr int BNm = S::BNm, GM = S::GM, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
     constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, NSTAGE = S::NSTAGE, CS_STRIDE = S::CS_STRIDE;
     constexpr int BROW = S::BROW, ADMA0 = S::ADMA0, ADMA1 = S::ADMA1, BDMA = S::BDMA;
     static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
+    constexpr size_t SLOT = (size_t)BM * S::BN;       // floats per part slot
+    static_assert(SLOT <= kGemmPartSlotFloats, "part slot larger than the workspace's");
+    static_assert(8 * FM * FN * 256 == (int)SLOT, "eight wavefronts' accumulators fill a slot");
     lds_char* lds = (lds_char*)smem;
     bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
+    int* flag = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + S::FLAG_OFF);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1070,14 +1080,31 @@ __device__ __forceinline__ void gemm_tiles_pp(
     const int a_rd = (row0 + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
     const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
+    // this wavefront's accumulators in a part slot (register layout, 16 bytes per lane per block)
+    const uint32_t wofs = (uint32_t)((wave * FM * FN * 256 + lane * 4) * 4);
 
-    for (long long w = first; w < total; w += G) {
+    static_assert(!(SPLIT && GATHER), "only the second projection splits");
+    float* const pbuf = SPLIT ? part_buf : nullptr;
+
+    // One work item: the whole K range (PART false), or part `part` of `nsplit` of the item
+    // whose parts use slot `slot` of the part buffer.  The full rounds and the split tail run
+    // in loops of their own, so the full rounds carry none of the split's state in registers.
+    auto run_item = [&](long long item, int part, int nsplit, int slot, auto split_tag)
+                        __attribute__((always_inline)) {
+        constexpr bool PART = decltype(split_tag)::value;
         int mt, nt;
-        item_coords(w, NT, tiles, mt, nt);
+        item_coords(item, NT, tiles, mt, nt);
+        mt = __builtin_amdgcn_readfirstlane(mt);
+        nt = __builtin_amdgcn_readfirstlane(nt);
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
         const bool rows_here = rows > row0;
+        int kt0 = 0, nsteps = KT;
+        if constexpr (PART) {
+            kt0 = __builtin_amdgcn_readfirstlane((int)((long long)part * KT / nsplit));
+            nsteps = __builtin_amdgcn_readfirstlane((int)((long long)(part + 1) * KT / nsplit) - kt0);
+        }
 
         const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, (uint32_t)(a_rows * K * 2))
                                                  : make_rsrc(A + (long long)tl.row0 * K, (uint32_t)rows * K * 2);
@@ -1092,13 +1119,42 @@ __device__ __forceinline__ void gemm_tiles_pp(
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         if (grp == 0)
-            pp_item<0, BM, NMAT, GATHER>(lds, KT, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows, wave,
-                                         lane, a_rd, b_rd, g, wn, acc);
+            pp_item<0, BM, NMAT, GATHER>(lds, kt0, nsteps, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
+                                         wave, lane, a_rd, b_rd, g, wn, acc);
         else
-            pp_item<1, BM, NMAT, GATHER>(lds, KT, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows, wave,
-                                         lane, a_rd, b_rd, g, wn, acc);
+            pp_item<1, BM, NMAT, GATHER>(lds, kt0, nsteps, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
+                                         wave, lane, a_rd, b_rd, g, wn, acc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
         __syncthreads();
+
+        // a split item: store this part; only the last part to arrive goes on, adding the
+        // parts in part order (the item's slots are consecutive in the part buffer)
+        __amdgpu_buffer_rsrc_t rp;
+        uint32_t wofs = 0;
+        if constexpr (PART) {
+            rp = make_rsrc(pbuf + (size_t)slot * nsplit * SLOT, (uint32_t)(nsplit * SLOT * 4));
+            wofs = (uint32_t)((wave * FM * FN * 256 + lane * 4) * 4);
+            if (rows_here) {
+                const uint32_t pofs = (uint32_t)(part * SLOT * 4);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        store_part(rp, pofs + wofs + (uint32_t)((fm * FN + fn) * 1024), acc[fm][fn]);
+            }
+            const SplitPart sp{nullptr, nullptr, part_cnt + slot, nsplit, SLOT};
+            if (!split_arrive(sp, flag)) return;
+        }
+        auto block = [&](int fm, int fn) -> f32x4_t {
+            if constexpr (!PART) {
+                return acc[fm][fn];
+            } else {
+                const uint32_t o = wofs + (uint32_t)((fm * FN + fn) * 1024);
+                f32x4_t sum = load_part(rp, o);
+                for (int q = 1; q < nsplit; ++q) sum += load_part(rp, o + (uint32_t)(q * SLOT * 4));
+                return sum;
+            }
+        };
 
         constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
         if (rows_here) {
@@ -1107,10 +1163,13 @@ __device__ __forceinline__ void gemm_tiles_pp(
 #pragma unroll
                 for (int fo = 0; fo < FO; ++fo) {
                     const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
+                    const f32x4_t x = block(fm, fo);
+                    f32x4_t u = x;
+                    if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        float val = acc[fm][fo][v];
-                        if constexpr (NMAT == 2) val = silu_f32(val) * acc[fm][fo + FN / 2][v];
+                        float val = x[v];
+                        if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
                         else if constexpr (ACT == 1) val = silu_f32(val);
                         const int r = row0 + 16 * fm + 4 * lq + v;
                         sC[r * CS_STRIDE + col] = f32_to_bf16(val);
@@ -1128,6 +1187,27 @@ __device__ __forceinline__ void gemm_tiles_pp(
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    // full rounds (every item when the launch does not split), then the split tail
+    long long main_end;
+    {
+        const WorkSplit wsp(total, G, pbuf ? KT : 0);
+        main_end = wsp.split == 1 ? total : wsp.full;
+    }
+    long long w = first;
+    for (; w < main_end; w += G) run_item(w, 0, 1, -1, std::false_type{});
+    if constexpr (SPLIT) {
+        // the split is derived again from the tile count (reloaded after the loop's memory
+        // clobbers), so that none of it is held through the full rounds
+        const WorkSplit wsp((long long)(*ntiles_p) * NT, G, pbuf ? KT : 0);
+        for (; w < wsp.nwork; w += G) {
+            long long item;
+            int part, slot;
+            wsp.item_of(w, item, part, slot);
+            run_item(item, __builtin_amdgcn_readfirstlane(part), wsp.split, __builtin_amdgcn_readfirstlane(slot),
+                     std::true_type{});
+        }
     }
 }
 
@@ -1138,16 +1218,19 @@ constexpr size_t pp_lds_bytes() { return PpShape<256, NMAT>::LDS_BYTES; }
 // 320-row kernel; whichever height the tile builder chose runs, the other returns.  (The
 // ping-pong form is faster where operands mostly hit in L2; on the weight stream from HBM
 // of 320-row tiles, whose reads come half a step later than in the 4-wavefront kernel,
-// it was slower.)
-template <int NMAT, int ACT, bool GATHER>
+// it was slower.)  The SPLIT instance also splits the last round along K; the host
+// launches it only where K allows a split, since the split's code alone slows the
+// kernel's short-K items by about 2%.
+template <int NMAT, int ACT, bool GATHER, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm_pp(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     extern __shared__ uint4 smem[];
     if (__builtin_amdgcn_readfirstlane(ntiles_p[1]) != 256) return;
-    gemm_tiles_pp<256, NMAT, ACT, GATHER>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows);
+    gemm_tiles_pp<256, NMAT, ACT, GATHER, SPLIT>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
+                                                 part_buf, part_cnt);
 }
 
 // ------------------------------------------------------------------------ tile list
@@ -1271,6 +1354,23 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
     return hipSuccess;
 }
 
+// The ping-pong kernel of a launch pair (256-row tiles), split-capable or not.
+template <int NMAT, int ACT, bool GATHER, bool SPLIT>
+static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
+                         const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
+                         long long max_items, int K, int N, const SplitBuffers& sb, hipStream_t st) {
+    static bool ready = false;
+    static int occ = 1;
+    unsigned G = 0;
+    constexpr size_t pp_bytes = pp_lds_bytes<NMAT>();
+    auto kpp = k_grouped_gemm_pp<NMAT, ACT, GATHER, SPLIT>;
+    hipError_t e = persistent_grid(kpp, pp_bytes, ready, occ, max_items, G, 512);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows, (const bf16_t*)B0,
+                       (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows, sb.parts, sb.counts);
+    return hipGetLastError();
+}
+
 template <int BM, int BMB, int NMAT, int WAVES_M, int ACT, bool GATHER>
 static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
                            const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
@@ -1289,15 +1389,12 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
         if constexpr (BM == 256 && BMB == 320) {
             // launch pair: 256-row tiles in the ping-pong kernel, 320-row tiles in the
             // 4-wavefront kernel; the one whose height was not chosen returns at once
-            static bool ready2 = false;
-            static int occ2 = 1;
-            constexpr size_t pp_bytes = pp_lds_bytes<NMAT>();
-            auto kpp = k_grouped_gemm_pp<NMAT, ACT, GATHER>;
-            hipError_t e = persistent_grid(kpp, pp_bytes, ready2, occ2, max_items, G, 512);
+            hipError_t e = (!GATHER && sb.parts && (K + 31) / 32 >= 2 * kMinPartSteps)
+                               ? run_pp<NMAT, ACT, GATHER, !GATHER>(A, a_rows, gather_rows, B0, B1, C, tiles, ntiles,
+                                                                    max_items, K, N, sb, st)
+                               : run_pp<NMAT, ACT, GATHER, false>(A, a_rows, gather_rows, B0, B1, C, tiles, ntiles,
+                                                                  max_items, K, N, sb, st);
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows,
-                               (const bf16_t*)B0, (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
             constexpr size_t lds_bytes = LdsShape<320, NMAT>::LDS_BYTES;
             auto kern = k_grouped_gemm_lds<320, 320, NMAT, ACT, GATHER>;
             e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);

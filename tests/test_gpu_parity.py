@@ -129,11 +129,13 @@ FFN_CASES = [  # T, H, E, k, F, ffn, dtype  (mean rows per expert picks the row 
     # ~275 rows per expert: the tile builder picks 320 x 192 tiles (8 items against ~16 x
     # the column blocks of 256-row tiles); ragged K and N against 192 (96 per SwiGLU matrix)
     (1100, 520, 8, 2, 392, "silu2", "bf16"), (1100, 264, 8, 2, 200, "swiglu", "bf16"),
-    # split of the last round along K (on 256 workgroups): 320-row tiles with 272 items in
-    # the first projection (16 left over, split in 2) and 24 in the second (split in 8),
-    # for both FFN kinds; 128-row tiles with ~384 items (split in 2) and ~48 (split in 5)
-    (1100, 520, 8, 2, 6400, "silu2", "bf16"), (1100, 520, 8, 2, 3200, "swiglu", "bf16"),
+    # split of the second projection's last round along K (on 256 workgroups, at least 64
+    # K steps of 32 per part): 320-row tiles with 24 items, split in 3 (K = 6400) and in 2
+    # (K = 4608); 128-row tiles with ~48 items, split in 2; 256-row tiles (the ping-pong
+    # kernel, ~512 rows per expert) with ~48 items, split in 2 (K = 4096 and 4608)
+    (1100, 520, 8, 2, 6400, "silu2", "bf16"), (1100, 520, 8, 2, 4608, "swiglu", "bf16"),
     (1024, 512, 16, 2, 4096, "silu2", "bf16"),
+    (2048, 512, 8, 2, 4096, "silu2", "bf16"), (2048, 512, 8, 2, 4608, "swiglu", "bf16"),
 ]
 
 
