@@ -22,20 +22,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// fp32 -> bf16 round-to-nearest-even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16 round-to-nearest-even (NaN kept quiet): gfx950's v_cvt_pk_bf16_f32, which
+// converts two values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
-// SiLU(z) = z / (1 + exp(-z)).  For z << 0, exp(-z) overflows to +inf and the
-// quotient is -0, the limit.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + exp(-z)), the quotient taken with the hardware reciprocal (1 ulp;
+// the result is rounded to bf16 afterwards).  For z << 0, exp(-z) overflows to +inf, its
+// reciprocal is 0 and the product -0, the limit.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = __lane_id();

@@ -1045,6 +1045,71 @@ __device__ __attribute__((always_inline)) inline void pp_item(
     pp_kloop<GROUP, BM, NMAT>(lds, kt0, KT, rows_here, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
 }
 
+// Output of one ping-pong work item: block(fm, fn) gives this wavefront's fp32 sums for
+// accumulator block (fm, fn); the activation is applied, rounded to bf16 and staged in LDS
+// (the K loop's stages are free by then), then written out as 16-byte row pieces.
+// C_rows: the item's first output row.
+template <int BM, int NMAT, int ACT, typename BlockFn>
+__device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, bool rows_here, int row0, int wn,
+                                             int l16, int lq, int tid, int rows, int n0, int N,
+                                             bf16_t* __restrict__ C_rows) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int FM = S::FM, FN = S::FN, BNm = S::BNm, WTN = S::WTN, CS_STRIDE = S::CS_STRIDE;
+    constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
+    typedef __attribute__((address_space(3))) bf16_t lds_bf16;
+    lds_bf16* sC = reinterpret_cast<lds_bf16*>(lds);
+    if (rows_here) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fo = 0; fo < FO; ++fo) {
+                const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
+                const f32x4_t x = block(fm, fo);
+                f32x4_t u = x;
+                if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float val = x[v];
+                    if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
+                    else if constexpr (ACT == 1) val = silu_f32(val);
+                    const int r = row0 + 16 * fm + 4 * lq + v;
+                    sC[r * CS_STRIDE + col] = f32_to_bf16(val);
+                }
+            }
+    }
+    __syncthreads();
+    constexpr int CPR = BNm / 8;
+    for (int c = tid; c < rows * CPR; c += 512) {
+        const int r = c / CPR, cc = c % CPR;
+        const int col = n0 + cc * 8;
+        if (col < N)
+            *reinterpret_cast<u32x4_t*>(C_rows + (long long)r * N + col) =
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sC + r * CS_STRIDE + cc * 8);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// The output of a split item's last part: the parts' sums, added in part order, through
+// pp_write_out.  Kept out of line so that the split tail's registers do not weigh on the
+// allocation of the kernel's K loops.
+template <int BM, int NMAT, int ACT>
+__device__ __attribute__((noinline)) void pp_write_split(lds_char* lds, __amdgpu_buffer_rsrc_t rp, uint32_t wofs,
+                                                         int nsplit, bool rows_here, int row0, int wn, int l16,
+                                                         int lq, int tid, int rows, int n0, int N,
+                                                         bf16_t* __restrict__ C_rows) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int FN = S::FN;
+    constexpr uint32_t SLOT_BYTES = (uint32_t)BM * S::BN * 4;
+    auto block = [&](int fm, int fn) -> f32x4_t {
+        const uint32_t o = wofs + (uint32_t)((fm * FN + fn) * 1024);
+        f32x4_t sum = load_part(rp, o);
+        for (int q = 1; q < nsplit; ++q) sum += load_part(rp, o + (uint32_t)q * SLOT_BYTES);
+        return sum;
+    };
+    pp_write_out<BM, NMAT, ACT>(lds, block, rows_here, row0, wn, l16, lq, tid, rows, n0, N, C_rows);
+}
+
 // All work items of one launch, ping-pong form.  part_buf / part_cnt as for gemm_tiles
 // (the split of the last round), used by the SPLIT instance only.
 template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
@@ -1145,48 +1210,12 @@ __device__ __forceinline__ void gemm_tiles_pp(
             const SplitPart sp{nullptr, nullptr, part_cnt + slot, nsplit, SLOT};
             if (!split_arrive(sp, flag)) return;
         }
-        auto block = [&](int fm, int fn) -> f32x4_t {
-            if constexpr (!PART) {
-                return acc[fm][fn];
-            } else {
-                const uint32_t o = wofs + (uint32_t)((fm * FN + fn) * 1024);
-                f32x4_t sum = load_part(rp, o);
-                for (int q = 1; q < nsplit; ++q) sum += load_part(rp, o + (uint32_t)(q * SLOT * 4));
-                return sum;
-            }
-        };
-
-        constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
-        if (rows_here) {
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fo = 0; fo < FO; ++fo) {
-                    const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
-                    const f32x4_t x = block(fm, fo);
-                    f32x4_t u = x;
-                    if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float val = x[v];
-                        if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
-                        else if constexpr (ACT == 1) val = silu_f32(val);
-                        const int r = row0 + 16 * fm + 4 * lq + v;
-                        sC[r * CS_STRIDE + col] = f32_to_bf16(val);
-                    }
-                }
-        }
-        __syncthreads();
-        constexpr int CPR = BNm / 8;
-        for (int c = tid; c < rows * CPR; c += 512) {
-            const int r = c / CPR, cc = c % CPR;
-            const int col = n0 + cc * 8;
-            if (col < N)
-                *reinterpret_cast<uint4*>(C + (long long)(tl.row0 + r) * N + col) =
-                    *reinterpret_cast<const uint4*>(sC + r * CS_STRIDE + cc * 8);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        if constexpr (PART)
+            pp_write_split<BM, NMAT, ACT>(lds, rp, wofs, nsplit, rows_here, row0, wn, l16, lq, tid, rows, n0, N,
+                                          C + (long long)tl.row0 * N);
+        else
+            pp_write_out<BM, NMAT, ACT>(lds, [&](int fm, int fn) { return acc[fm][fn]; }, rows_here, row0, wn, l16,
+                                        lq, tid, rows, n0, N, C + (long long)tl.row0 * N);
     };
 
     // full rounds (every item when the launch does not split), then the split tail
