@@ -339,20 +339,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <int BM, int NMAT>
 struct LdsShape {
     static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, WAVES_M = 2, WAVES_N = 2, BK = 32;
-    // 320-row tiles keep W rows 192 wide in LDS (the columns they use), which makes room
-    // for a fifth stage: 5 x 32 KB = 160 KB
-    static constexpr int NSTAGE = BM == 320 ? 5 : 4, LBN = BM == 320 ? 192 : 256, LBNm = LBN / NMAT;
+    // A and W stages sit in rings of their own, NA and NW stages deep: the DMA of a step's
+    // A runs NA - 1 steps ahead of its use, its W NW - 1 steps.  320-row tiles stream each
+    // expert's weights from HBM once; their W runs 7 steps ahead (8 x 12 KB) against 2 for
+    // A, which comes from L2 (3 x 20 KB), to keep enough weight bytes in flight for HBM's
+    // latency.  They keep W rows 192 wide in LDS (the columns they use).
+    static constexpr int NA = BM == 320 ? 3 : 4, NW = BM == 320 ? 8 : 4;
+    static constexpr int LBN = BM == 320 ? 192 : 256, LBNm = LBN / NMAT;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
-    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2, STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2;
+    static constexpr int W_RING = NA * A_STAGE;       // LDS offset of the W ring
     static constexpr int ADMA = A_STAGE / 1024 / 4;   // A DMA instructions per wavefront per step
     static constexpr int BDMA = B_STAGE / 1024 / 4;   // W DMA instructions per wavefront per step
     static constexpr int DPW = ADMA + BDMA;
     static constexpr int BROW = 2 * LBNm;             // LDS bytes per W row
     static constexpr int BMAT_DMA = B_STAGE / 1024 / NMAT;   // W DMA instructions per matrix
     static constexpr int CS_STRIDE = BNm + 8;
-    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)BM * CS_STRIDE * 2
-                                            ? (size_t)NSTAGE * STAGE : (size_t)BM * CS_STRIDE * 2;
+    static constexpr size_t RING_BYTES = (size_t)NA * A_STAGE + (size_t)NW * B_STAGE;
+    static constexpr size_t LDS_BYTES = RING_BYTES > (size_t)BM * CS_STRIDE * 2 ? RING_BYTES
+                                                                                : (size_t)BM * CS_STRIDE * 2;
+    // Each step issues its A DMA (for step + NA - 1), then its W DMA (for step + NW - 1).
+    // Before step r, A(r) and W(r) must have landed; loads complete in issue order, so the
+    // wait is for the later-issued of the two: A(r) (issued NA - 1 steps back, followed by
+    // its own step's W and NA - 2 more steps) when NW > NA, else W(r).
+    static constexpr int VMCNT = NW > NA ? BDMA + (NA - 2) * DPW : (NW - 2) * DPW;
+    static_assert(NW >= NA && NA >= 2, "the W ring is at least as deep as the A ring");
+    static_assert((NW - 1) * DPW < 64, "DMA in flight fits the 6-bit vmcnt");
 };
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Per-tile DMA description (one wavefront's share of a K step).
 template <int ADMA, int BDMA>
@@ -362,19 +378,30 @@ struct DmaPlan {                 // (the buffer resources travel as separate arg
     uint32_t b_off[BDMA];        // byte offset at k0 = 0 (kOOB: column past N)
 };
 
+// This wavefront's share of the A DMA of K step kt into the A stage `dst`; `dummy` loads
+// zeros (the prologue's placeholders, which keep every step's DMA count the same).
 template <int BM, int NMAT>
-__device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
-                                         __amdgpu_buffer_rsrc_t rb1,
-                                         const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
-                                         int kt, int K, uint32_t rowB, int wave) {
+__device__ __forceinline__ void dma_a(lds_char* dst, __amdgpu_buffer_rsrc_t ra,
+                                      const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                      int kt, int K, int wave, bool dummy = false) {
     using S = LdsShape<BM, NMAT>;
-    constexpr int ADMA = S::ADMA, BDMA = S::BDMA;
+    constexpr int ADMA = S::ADMA;
     const uint32_t k0 = (uint32_t)kt * S::BK;
 #pragma unroll
     for (int i = 0; i < ADMA; ++i) {
-        const uint32_t off = (k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
+        const uint32_t off = (!dummy && k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (wave * ADMA + i) * 1024), 16, off, 0, 0, 0);
     }
+}
+
+// This wavefront's share of the W DMA of K step kt into the W stage `dst`.
+template <int BM, int NMAT>
+__device__ __forceinline__ void dma_w(lds_char* dst, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+                                      const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                      int kt, uint32_t rowB, int wave) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int BDMA = S::BDMA;
+    const uint32_t k0 = (uint32_t)kt * S::BK;
 #pragma unroll
     for (int i = 0; i < BDMA; ++i) {
         const int j = wave * BDMA + i;
@@ -383,7 +410,39 @@ __device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t r
         const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
         constexpr int per_mat = S::BMAT_DMA;   // instructions of the first matrix
         const __amdgpu_buffer_rsrc_t rb = (NMAT == 2 && j >= per_mat) ? rb1 : rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + j * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+// One step's DMA: A of step r + NA - 1 and W of step r + NW - 1 (r relative to the first
+// step kt0 of the work, absolute step kt0 + r), each into the stage its ring holds for it
+// (the stage of step r - 1, free once every wavefront has passed step r's barrier).
+template <int BM, int NMAT>
+__device__ __forceinline__ void dma_step(lds_char* lds, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                         __amdgpu_buffer_rsrc_t rb1,
+                                         const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                         int kt0, int r, int K, uint32_t rowB, int wave) {
+    using S = LdsShape<BM, NMAT>;
+    const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
+    dma_a<BM, NMAT>(lds + (ra_step % S::NA) * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave);
+    dma_w<BM, NMAT>(lds + S::W_RING + (rw_step % S::NW) * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
+}
+
+// The DMA ahead of a work's first step, issued as the steps -(NW - 1) .. -1 would have
+// issued it, so that the first steps wait with the same count as the rest: A of steps
+// below 0 is a zero-loading placeholder.
+template <int BM, int NMAT>
+__device__ __forceinline__ void dma_prologue(lds_char* lds, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                             __amdgpu_buffer_rsrc_t rb1,
+                                             const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                             int kt0, int K, uint32_t rowB, int wave) {
+    using S = LdsShape<BM, NMAT>;
+#pragma unroll
+    for (int r = -(S::NW - 1); r < 0; ++r) {
+        const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
+        const int aslot = ((ra_step % S::NA) + S::NA) % S::NA;
+        dma_a<BM, NMAT>(lds + aslot * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave, ra_step < 0);
+        dma_w<BM, NMAT>(lds + S::W_RING + rw_step * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
     }
 }
 
@@ -399,15 +458,13 @@ __device__ __forceinline__ void dma_step(lds_char* dst, __amdgpu_buffer_rsrc_t r
 // multiplied.
 template <int BM, int NMAT, int FMA>
 __device__ __attribute__((always_inline)) inline void kstep(
-    const lds_char* __restrict__ cur, lds_char* __restrict__ nxt, __amdgpu_buffer_rsrc_t ra,
-    __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
-    const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int kt_dma, int K, uint32_t rowB,
+    const lds_char* __restrict__ As, const lds_char* __restrict__ Bs, lds_char* __restrict__ lds,
+    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int kt0, int r, int K, uint32_t rowB,
     int wave, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN]) {
     using S = LdsShape<BM, NMAT>;
     constexpr int FM = FMA, FN = S::FN, BROW = S::BROW;
-    const lds_char* As = cur;
-    const lds_char* Bs = cur + S::A_STAGE;
     // Every fragment read of the step is issued before its first MFMA (A row block 0,
     // then the B columns, then the other A row blocks, in the order the MFMAs use them),
     // so the MFMAs wait on the LDS counter step by step instead of paying the LDS
@@ -436,7 +493,7 @@ __device__ __attribute__((always_inline)) inline void kstep(
 #pragma unroll
     for (int fm = 1; fm < FM; ++fm) read_a(fm);
     __builtin_amdgcn_sched_barrier(0);
-    dma_step<BM, NMAT>(nxt, ra, rb0, rb1, pl, kt_dma, K, rowB, wave);
+    dma_step<BM, NMAT>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -460,24 +517,23 @@ __device__ __forceinline__ void wait_dma(int pending);
 __device__ __forceinline__ void kloop_barrier();
 
 // The K loop of one work item for a wavefront whose rows fill FMA 16-row blocks: KT
-// steps starting at step kt0 (the DMA of steps kt0 .. kt0 + NSTAGE - 2 is in flight).
+// steps starting at step kt0 (dma_prologue has issued the DMA ahead of the first).
 template <int BM, int NMAT, int FMA>
 __device__ __attribute__((always_inline)) inline void kloop(
     lds_char* lds, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K, uint32_t rowB, int wave,
     int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN], int kt0) {
     using S = LdsShape<BM, NMAT>;
-    constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE;
-    for (int kt = 0; kt < KT; ++kt) {
-        wait_dma<S::DPW>(NSTAGE - 2);
+    for (int r = 0; r < KT; ++r) {
+        wait_vmcnt<S::VMCNT>();
         kloop_barrier();
-        kstep<BM, NMAT, FMA>(lds + (kt % NSTAGE) * STAGE, lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE,
-                             ra, rb0, rb1, pl, kt0 + kt + NSTAGE - 1, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+        kstep<BM, NMAT, FMA>(lds + (r % S::NA) * S::A_STAGE, lds + S::W_RING + (r % S::NW) * S::B_STAGE, lds,
+                             ra, rb0, rb1, pl, kt0, r, K, rowB, wave, a_rd, b_rd, g, wn, acc);
     }
 }
 
 // Workgroup barrier of the K loop.  Each wavefront has already waited for its own DMA
-// of the step (wait_dma) and its fragment reads of the previous step were consumed by
+// of the step (wait_vmcnt) and its fragment reads of the previous step were consumed by
 // MFMAs before it arrives, so the barrier alone makes the stage complete for all and the
 // stage being refilled free.  It is written without __syncthreads' memory fence, which
 // otherwise leads the compiler to drain every DMA in flight (vmcnt(0)) at each step; the
@@ -665,8 +721,8 @@ __device__ __forceinline__ void gemm_tiles(
     long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     using S = LdsShape<BM, NMAT>;
     constexpr int BNm = S::BNm, WAVES_N = S::WAVES_N, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
-    constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, ADMA = S::ADMA, BDMA = S::BDMA;
-    constexpr int NSTAGE = S::NSTAGE, CS_STRIDE = S::CS_STRIDE, BROW = S::BROW;
+    constexpr int FM = S::FM, FN = S::FN, ADMA = S::ADMA, BDMA = S::BDMA;
+    constexpr int CS_STRIDE = S::CS_STRIDE, BROW = S::BROW;
     static_assert(ADMA >= 1 && BDMA >= 1, "every wavefront moves part of each operand");
     static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
 
@@ -745,7 +801,8 @@ __device__ __forceinline__ void gemm_tiles(
             long long row = tl.row0 + min(r, rows - 1);
             if constexpr (GATHER) row = gather_rows[row];
             else row -= tl.row0;
-            pl.a_off[i] = (uint32_t)(row * K * 2) + (uint32_t)(q * 16);
+            // rows past the tile's own load nothing (zeros through the buffer bound)
+            pl.a_off[i] = r < rows ? (uint32_t)(row * K * 2) + (uint32_t)(q * 16) : kOOB;
         }
         const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, (uint32_t)(a_rows * K * 2))
                                                  : make_rsrc(A + (long long)tl.row0 * K, (uint32_t)rows * K * 2);
@@ -775,10 +832,8 @@ __device__ __forceinline__ void gemm_tiles(
             pl.b_off[i] = (8 * c < BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
         }
 
-        // prologue: steps kt0..kt0+NSTAGE-2 in flight (steps past K read zeros, see kstep)
-#pragma unroll
-        for (int t = 0; t < NSTAGE - 1; ++t)
-            dma_step<BM, NMAT>(lds + t * STAGE, ra, rb0, rb1, pl, kt0 + t, K, rowB, wave);
+        // prologue: the DMA ahead of the first step (steps past K read zeros, see kstep)
+        dma_prologue<BM, NMAT>(lds, ra, rb0, rb1, pl, kt0, K, rowB, wave);
         bool write_out;       // the same in every wavefront of the workgroup
         if (wave_rows) {
             // a wavefront whose rows fill only the first blocks of its tile multiplies just
@@ -794,11 +849,10 @@ __device__ __forceinline__ void gemm_tiles(
             else write_out = MOE_ROWS_ITEM(FM);
 #undef MOE_ROWS_ITEM
         } else {       // no rows for this wavefront: it still moves its share of the tiles
-            for (int kt = 0; kt < nsteps; ++kt) {
-                wait_dma<S::DPW>(NSTAGE - 2);
+            for (int r = 0; r < nsteps; ++r) {
+                wait_vmcnt<S::VMCNT>();
                 kloop_barrier();
-                dma_step<BM, NMAT>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl,
-                                   kt0 + kt + NSTAGE - 1, K, rowB, wave);
+                dma_step<BM, NMAT>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
@@ -927,7 +981,7 @@ __device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& p
         long long row = tl.row0 + min(r, rows - 1);
         if constexpr (GATHER) row = gather_rows[row];
         else row -= tl.row0;
-        pl.a_off[i] = (uint32_t)(row * K * 2) + (uint32_t)(q * 16);
+        pl.a_off[i] = r < rows ? (uint32_t)(row * K * 2) + (uint32_t)(q * 16) : kOOB;
     }
 #pragma unroll
     for (int i = 0; i < S::BDMA; ++i) {
