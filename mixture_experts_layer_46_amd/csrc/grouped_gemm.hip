@@ -904,40 +904,56 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
 
 // ------------------------------------------- ping-pong variant (two wavefront groups)
 // Same tiles, LDS layout and DMA as above, with 8 wavefronts per workgroup in two groups
-// of four (one wavefront of each group per SIMD, 128 accumulator registers each).  Each K
-// step has a read phase (DMA issue and fragment reads) and an MFMA phase; the groups run
-// them out of step, so one group's LDS reads and DMA issue overlap the other group's
-// MFMAs.  Between two consecutive barriers one group is in its read phase and the other
-// in its MFMA phase:
+// of four (one wavefront of each group per SIMD, at most 128 accumulator registers each).
+// Each K step has a read phase (DMA issue and fragment reads) and an MFMA phase; the
+// groups run them out of step, so one group's LDS reads and DMA issue overlap the other
+// group's MFMAs.  Between two consecutive barriers one group is in its read phase and the
+// other in its MFMA phase:
 //   group 0:  R0 | M0 | R1 | M1 | ... | M(KT-1) | (idle)
 //   group 1: (idle) | R0 | M0 | R1 | ... | R(KT-1) | M(KT-1)
 // Both groups therefore pass 2 KT + 1 barriers per item (plus the prologue's).
-//   * Stage k is read in group 0's phase 2k and group 1's phase 2k+1.  Every wavefront
-//     waits for its own DMA of stage k before barrier 2k-1 (group 0 at the end of M(k-1),
-//     group 1 at the end of R(k-1)), so all of stage k has landed when it is read.
-//   * R(k) starts the DMA of stage k+3 into the slot of stage k-1.  Each read phase ends
-//     with lgkmcnt(0) before its barrier, so both groups' reads of stage k-1 (phases 2k-2
-//     and 2k-1) are complete before either group issues that DMA (phases 2k and 2k+1).
+//   * Step k is read in group 0's phase 2k and group 1's phase 2k+1.  Every wavefront
+//     waits for its own DMA of step k before barrier 2k-1 (group 0 at the end of M(k-1),
+//     group 1 at the end of R(k-1)), so all of step k has landed when it is read.
+//   * R(k) starts the DMA of A for step k + NA - 1 and of W for step k + NW - 1, each into
+//     the stage of its ring that held step k - 1.  Each read phase ends with lgkmcnt(0)
+//     before its barrier, so both groups' reads of step k-1 (phases 2k-2 and 2k-1) are
+//     complete before either group issues that DMA (phases 2k and 2k+1).
 template <int BM, int NMAT>
 struct PpShape {
-    static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, BK = 32, NSTAGE = 4;
-    static constexpr int LBN = 256, LBNm = LBN / NMAT;
+    static constexpr int BN = BM == 320 ? 192 : 256, BNm = BN / NMAT, BK = 32;
+    // W rows in LDS: 256 columns (512-byte rows, 16-byte chunk swizzle fk), or for 320-row
+    // tiles the 192 columns they use (swizzle fk320), as in the 4-wavefront kernel
+    static constexpr int LBN = BM == 320 ? 192 : 256, LBNm = LBN / NMAT;
+    // ring depths: 320-row tiles stream their weights from HBM, 7 steps ahead
+    static constexpr int NA = BM == 320 ? 3 : 4, NW = BM == 320 ? 8 : 4;
     static constexpr int GM = BM / 2;                        // rows of one group
     static constexpr int WTM = GM / 2, WTN = BN / 2;         // wavefront tile (2 x 2 per group)
     static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2, STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2;
+    static constexpr int W_RING = NA * A_STAGE;              // LDS offset of the W ring
     static constexpr int A_INSTR = A_STAGE / 1024, B_INSTR = B_STAGE / 1024;
-    // A instruction j goes to wavefront j % 8: group 0 (wavefronts 0-3) may take one more
+    static constexpr int BMAT_DMA = B_INSTR / NMAT;          // W instructions per matrix
+    // A instruction j goes to wavefront j % 8: group 0 (wavefronts 0-3) may take one more.
+    // W instructions: BDMA0 per group-0 wavefront, then BDMA1 per group-1 wavefront, so
+    // that both groups issue DPW instructions per step.
     static constexpr int ADMA0 = (A_INSTR + 7 - 0) / 8, ADMA1 = (A_INSTR + 7 - 4) / 8;
-    static constexpr int BDMA = B_INSTR / 8;
-    static constexpr int DPW0 = ADMA0 + BDMA, DPW1 = ADMA1 + BDMA;
+    static constexpr int DPW = (A_INSTR + B_INSTR) / 8;
+    static constexpr int BDMA0 = DPW - ADMA0, BDMA1 = DPW - ADMA1;
     static constexpr int BROW = 2 * LBNm, CS_STRIDE = BNm + 8;
+    // the wait before a step, per group: see LdsShape::VMCNT
+    template <int GROUP>
+    static constexpr int vmcnt() {
+        return NW > NA ? (GROUP == 0 ? BDMA0 : BDMA1) + (NA - 2) * DPW : (NW - 2) * DPW;
+    }
     // the split parts' arrival flag: an LDS word past the output staging tile
     static constexpr int FLAG_OFF = (BM * CS_STRIDE * 2 + 15) / 16 * 16;
-    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE > (size_t)FLAG_OFF + 16
-                                            ? (size_t)NSTAGE * STAGE : (size_t)FLAG_OFF + 16;
+    static constexpr size_t RING_BYTES = (size_t)NA * A_STAGE + (size_t)NW * B_STAGE;
+    static constexpr size_t LDS_BYTES = RING_BYTES > (size_t)FLAG_OFF + 16 ? RING_BYTES : (size_t)FLAG_OFF + 16;
     static_assert(A_INSTR % 8 == 0 || A_INSTR % 8 == 4, "A instructions split by groups");
-    static_assert(B_INSTR % 8 == 0, "W instructions split evenly");
+    static_assert((A_INSTR + B_INSTR) % 8 == 0 && BDMA0 >= 1 && BDMA1 >= 1, "DMA split evenly by wavefronts");
+    static_assert(4 * BDMA0 + 4 * BDMA1 == B_INSTR, "every W instruction has a wavefront");
+    static_assert(NW >= NA && NA >= 2 && (NW - 1) * DPW < 64, "ring depths");
 };
 
 template <int ADMA, int BDMA>
@@ -945,33 +961,69 @@ struct PpPlan {
     uint32_t a_off[ADMA], a_k[ADMA], b_off[BDMA];
 };
 
-// This wavefront's share of one stage's DMA (ADMA A and BDMA W instructions).
-template <int BM, int NMAT, int ADMA>
-__device__ __forceinline__ void pp_dma(lds_char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
-                                       __amdgpu_buffer_rsrc_t rb1, const PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& pl,
-                                       int kt, int K, uint32_t rowB, int wave) {
+template <int BM, int NMAT, int GROUP>
+using PpPlanOf = PpPlan<GROUP == 0 ? PpShape<BM, NMAT>::ADMA0 : PpShape<BM, NMAT>::ADMA1,
+                        GROUP == 0 ? PpShape<BM, NMAT>::BDMA0 : PpShape<BM, NMAT>::BDMA1>;
+
+// First W instruction of a wavefront (wavefronts of group 0 take BDMA0 each, then group 1).
+template <int BM, int NMAT, int GROUP>
+__device__ __forceinline__ int pp_w_first(int wave) {
     using S = PpShape<BM, NMAT>;
+    return GROUP == 0 ? wave * S::BDMA0 : 4 * S::BDMA0 + (wave - 4) * S::BDMA1;
+}
+
+// This wavefront's share of the A DMA of K step kt into A stage `dst` (`dummy`: zeros).
+template <int BM, int NMAT, int GROUP>
+__device__ __forceinline__ void pp_dma_a(lds_char* dst, __amdgpu_buffer_rsrc_t ra,
+                                         const PpPlanOf<BM, NMAT, GROUP>& pl, int kt, int K, int wave,
+                                         bool dummy = false) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1;
     const uint32_t k0 = (uint32_t)kt * S::BK;
 #pragma unroll
     for (int i = 0; i < ADMA; ++i) {
-        const uint32_t off = (k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
+        const uint32_t off = (!dummy && k0 + pl.a_k[i] < (uint32_t)K) ? pl.a_off[i] + k0 * 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst + (wave + 8 * i) * 1024), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < S::BDMA; ++i) {
-        const int j = wave * S::BDMA + i;
-        const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && j >= 8) ? rb1 : rb0,
-                                                 (lds_void*)(dst + S::A_STAGE + j * 1024), 16, off, 0, 0, 0);
     }
 }
 
-// DMA plan of one wavefront for one tile: A instruction j = wave + 8 i covers 16 rows x
-// 4 chunks; W instruction j = wave * BDMA + i as in the 4-wavefront kernel.
-template <int BM, int NMAT, int ADMA, bool GATHER>
-__device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& pl, const Tile& tl, int rows, int n0,
-                                        int K, int N, const int32_t* __restrict__ gather_rows, int wave, int lane) {
+// This wavefront's share of the W DMA of K step kt into W stage `dst`.
+template <int BM, int NMAT, int GROUP>
+__device__ __forceinline__ void pp_dma_w(lds_char* dst, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+                                         const PpPlanOf<BM, NMAT, GROUP>& pl, int kt, uint32_t rowB, int wave) {
     using S = PpShape<BM, NMAT>;
+    constexpr int BDMA = GROUP == 0 ? S::BDMA0 : S::BDMA1;
+    const uint32_t k0 = (uint32_t)kt * S::BK;
+    const int j0 = pp_w_first<BM, NMAT, GROUP>(wave);
+#pragma unroll
+    for (int i = 0; i < BDMA; ++i) {
+        const int j = j0 + i;
+        const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
+        const __amdgpu_buffer_rsrc_t rb = (NMAT == 2 && j >= S::BMAT_DMA) ? rb1 : rb0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + j * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+// One read phase's DMA: A of step r + NA - 1 and W of step r + NW - 1 (r relative to the
+// work's first step kt0), each into the stage its ring held for step r - 1.
+template <int BM, int NMAT, int GROUP>
+__device__ __forceinline__ void pp_dma_step(lds_char* lds, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                            __amdgpu_buffer_rsrc_t rb1, const PpPlanOf<BM, NMAT, GROUP>& pl,
+                                            int kt0, int r, int K, uint32_t rowB, int wave) {
+    using S = PpShape<BM, NMAT>;
+    const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
+    pp_dma_a<BM, NMAT, GROUP>(lds + (ra_step % S::NA) * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave);
+    pp_dma_w<BM, NMAT, GROUP>(lds + S::W_RING + (rw_step % S::NW) * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step,
+                              rowB, wave);
+}
+
+// DMA plan of one wavefront for one tile: A instruction j = wave + 8 i covers 16 rows x
+// 4 chunks; W instruction j (from pp_w_first) is placed as in the 4-wavefront kernel.
+template <int BM, int NMAT, int GROUP, bool GATHER>
+__device__ __forceinline__ void pp_plan(PpPlanOf<BM, NMAT, GROUP>& pl, const Tile& tl, int rows, int n0, int K,
+                                        int N, const int32_t* __restrict__ gather_rows, int wave, int lane) {
+    using S = PpShape<BM, NMAT>;
+    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1, BDMA = GROUP == 0 ? S::BDMA0 : S::BDMA1;
     const uint32_t rowB = (uint32_t)N * 2;
 #pragma unroll
     for (int i = 0; i < ADMA; ++i) {
@@ -983,11 +1035,16 @@ __device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& p
         else row -= tl.row0;
         pl.a_off[i] = r < rows ? (uint32_t)(row * K * 2) + (uint32_t)(q * 16) : kOOB;
     }
+    const int j0 = pp_w_first<BM, NMAT, GROUP>(wave);
 #pragma unroll
-    for (int i = 0; i < S::BDMA; ++i) {
-        const int j = wave * S::BDMA + i;
+    for (int i = 0; i < BDMA; ++i) {
+        const int j = j0 + i;
         int k, c;
-        if constexpr (NMAT == 1) {
+        if constexpr (BM == 320) {
+            const int pos = (j % S::BMAT_DMA) * 1024 + lane * 16;   // byte within the matrix
+            k = pos / S::BROW;
+            c = ((pos % S::BROW) / 16) ^ (2 * fk320<NMAT>(k));
+        } else if constexpr (NMAT == 1) {
             k = j * 2 + (lane >> 5);
             c = (lane & 31) ^ fk(k);
         } else {
@@ -999,24 +1056,15 @@ __device__ __forceinline__ void pp_plan(PpPlan<ADMA, PpShape<BM, NMAT>::BDMA>& p
     }
 }
 
-// The whole K loop of one work item for group GROUP: plan, prologue, loop.
-template <int GROUP, int BM, int NMAT, bool GATHER>
-__device__ __attribute__((always_inline)) inline void pp_item(
-    lds_char* lds, int kt0, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
-    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
-    const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
-    f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]);
-
 template <int BM, int NMAT>
-__device__ __forceinline__ void pp_read(const lds_char* st, int a_rd, int b_rd, int g, int wn,
+__device__ __forceinline__ void pp_read(const lds_char* As, const lds_char* Bs, int a_rd, int b_rd, int g, int wn,
                                         bf16x8_t (&af)[PpShape<BM, NMAT>::FM],
                                         bf16x8_t (&bfr)[PpShape<BM, NMAT>::FN]) {
     using S = PpShape<BM, NMAT>;
     constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
-    const lds_char* Bs = st + S::A_STAGE;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(st + a_rd + fm * 16 * S::BK * 2);
+        af[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(As + a_rd + fm * 16 * S::BK * 2);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         int mat, blk;
@@ -1036,36 +1084,34 @@ __device__ __forceinline__ void pp_read(const lds_char* st, int a_rd, int b_rd, 
 }
 
 // The K loop of one group (see the phase table above) over K steps kt0 .. kt0 + KT - 1.
-// `rows_here`: the wavefront has rows of the tile (else it only moves its DMA share and
-// keeps the barriers).
+// `nblk`: the wavefront's 16-row blocks that hold rows of the tile (only they are
+// multiplied; with none the wavefront only moves its DMA share and keeps the barriers).
 template <int GROUP, int BM, int NMAT>
 __device__ __attribute__((always_inline)) inline void pp_kloop(
-    lds_char* lds, int kt0, int KT, bool rows_here, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
-    __amdgpu_buffer_rsrc_t rb1,
-    const PpPlan<GROUP == 0 ? PpShape<BM, NMAT>::ADMA0 : PpShape<BM, NMAT>::ADMA1, PpShape<BM, NMAT>::BDMA>& pl,
-    int K, uint32_t rowB, int wave, int a_rd, int b_rd, int g, int wn,
-    f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
+    lds_char* lds, int kt0, int KT, int nblk, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+    __amdgpu_buffer_rsrc_t rb1, const PpPlanOf<BM, NMAT, GROUP>& pl, int K, uint32_t rowB, int wave, int a_rd,
+    int b_rd, int g, int wn, f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
     using S = PpShape<BM, NMAT>;
-    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1;
-    constexpr int DPW = ADMA + S::BDMA;
-    constexpr int NSTAGE = S::NSTAGE, STAGE = S::STAGE, FM = S::FM, FN = S::FN;
+    constexpr int FM = S::FM, FN = S::FN, VMCNT = S::template vmcnt<GROUP>();
     bf16x8_t af[FM], bfr[FN];
     if constexpr (GROUP == 1) kloop_barrier();                  // group 1's idle first phase
     for (int kt = 0; kt < KT; ++kt) {
-        // read phase: DMA of stage kt + 3 into the slot of stage kt - 1, fragments of stage kt
-        pp_dma<BM, NMAT, ADMA>(lds + ((kt + NSTAGE - 1) % NSTAGE) * STAGE, ra, rb0, rb1, pl, kt0 + kt + NSTAGE - 1,
-                               K, rowB, wave);
-        if (rows_here) pp_read<BM, NMAT>(lds + (kt % NSTAGE) * STAGE, a_rd, b_rd, g, wn, af, bfr);
+        // read phase: DMA of the steps NA - 1 and NW - 1 ahead, fragments of step kt
+        pp_dma_step<BM, NMAT, GROUP>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
+        // (read by every wavefront: a branch here makes the compiler copy the fragments)
+        pp_read<BM, NMAT>(lds + (kt % S::NA) * S::A_STAGE, lds + S::W_RING + (kt % S::NW) * S::B_STAGE, a_rd, b_rd,
+                          g, wn, af, bfr);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if constexpr (GROUP == 1) wait_dma<DPW>(2);              // stage kt + 1 complete
+        if constexpr (GROUP == 1) wait_vmcnt<VMCNT>();           // step kt + 1 complete
         kloop_barrier();
         // MFMA phase
-        if (rows_here) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+        for (int fm = 0; fm < FM; ++fm) {
+            if (fm < nblk) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            }
         }
         // the accumulators live in AGPRs (at two wavefronts per SIMD the compiler would
         // otherwise keep them in VGPRs, next to the fragments, and spill)
@@ -1073,30 +1119,35 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-        if constexpr (GROUP == 0) wait_dma<DPW>(2);              // stage kt + 1 complete
+        if constexpr (GROUP == 0) wait_vmcnt<VMCNT>();           // step kt + 1 complete
         kloop_barrier();
     }
     if constexpr (GROUP == 0) kloop_barrier();                  // group 0's idle last phase
 }
 
+// The whole K loop of one work item for group GROUP: plan, prologue, loop.  The prologue
+// issues the DMA as the steps -(NW - 1) .. -1 would have (A of steps below 0 as zero
+// placeholders), so the first steps wait with the same count as the rest.
 template <int GROUP, int BM, int NMAT, bool GATHER>
 __device__ __attribute__((always_inline)) inline void pp_item(
-    lds_char* lds, int kt0, int KT, bool rows_here, const Tile& tl, int rows, int n0, int K, int N,
+    lds_char* lds, int kt0, int KT, int nblk, const Tile& tl, int rows, int n0, int K, int N,
     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
     const int32_t* __restrict__ gather_rows, int wave, int lane, int a_rd, int b_rd, int g, int wn,
     f32x4_t (&acc)[PpShape<BM, NMAT>::FM][PpShape<BM, NMAT>::FN]) {
     using S = PpShape<BM, NMAT>;
-    constexpr int ADMA = GROUP == 0 ? S::ADMA0 : S::ADMA1;
     const uint32_t rowB = (uint32_t)N * 2;
-    PpPlan<ADMA, S::BDMA> pl;
-    pp_plan<BM, NMAT, ADMA, GATHER>(pl, tl, rows, n0, K, N, gather_rows, wave, lane);
-    // prologue: stages 0..2 in flight, stage 0 complete for all before the first reads
+    PpPlanOf<BM, NMAT, GROUP> pl;
+    pp_plan<BM, NMAT, GROUP, GATHER>(pl, tl, rows, n0, K, N, gather_rows, wave, lane);
 #pragma unroll
-    for (int t = 0; t < S::NSTAGE - 1; ++t)
-        pp_dma<BM, NMAT, ADMA>(lds + t * S::STAGE, ra, rb0, rb1, pl, kt0 + t, K, rowB, wave);
-    wait_dma<ADMA + S::BDMA>(2);
+    for (int r = -(S::NW - 1); r < 0; ++r) {
+        const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
+        const int aslot = ((ra_step % S::NA) + S::NA) % S::NA;
+        pp_dma_a<BM, NMAT, GROUP>(lds + aslot * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave, ra_step < 0);
+        pp_dma_w<BM, NMAT, GROUP>(lds + S::W_RING + rw_step * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
+    }
+    wait_vmcnt<S::template vmcnt<GROUP>()>();                    // step 0 complete for all
     kloop_barrier();
-    pp_kloop<GROUP, BM, NMAT>(lds, kt0, KT, rows_here, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+    pp_kloop<GROUP, BM, NMAT>(lds, kt0, KT, nblk, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
 }
 
 // Output of one ping-pong work item: block(fm, fn) gives this wavefront's fp32 sums for
@@ -1104,7 +1155,7 @@ __device__ __attribute__((always_inline)) inline void pp_item(
 // (the K loop's stages are free by then), then written out as 16-byte row pieces.
 // C_rows: the item's first output row.
 template <int BM, int NMAT, int ACT, typename BlockFn>
-__device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, bool rows_here, int row0, int wn,
+__device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, int nblk, int row0, int wn,
                                              int l16, int lq, int tid, int rows, int n0, int N,
                                              bf16_t* __restrict__ C_rows) {
     using S = PpShape<BM, NMAT>;
@@ -1112,24 +1163,24 @@ __device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, bool 
     constexpr int FO = (NMAT == 2) ? FN / 2 : FN;
     typedef __attribute__((address_space(3))) bf16_t lds_bf16;
     lds_bf16* sC = reinterpret_cast<lds_bf16*>(lds);
-    if (rows_here) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+        if (fm >= nblk) break;                 // blocks past the wavefront's rows
 #pragma unroll
-            for (int fo = 0; fo < FO; ++fo) {
-                const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
-                const f32x4_t x = block(fm, fo);
-                f32x4_t u = x;
-                if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
+        for (int fo = 0; fo < FO; ++fo) {
+            const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
+            const f32x4_t x = block(fm, fo);
+            f32x4_t u = x;
+            if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float val = x[v];
-                    if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
-                    else if constexpr (ACT == 1) val = silu_f32(val);
-                    const int r = row0 + 16 * fm + 4 * lq + v;
-                    sC[r * CS_STRIDE + col] = f32_to_bf16(val);
-                }
+            for (int v = 0; v < 4; ++v) {
+                float val = x[v];
+                if constexpr (NMAT == 2) val = silu_f32(val) * u[v];
+                else if constexpr (ACT == 1) val = silu_f32(val);
+                const int r = row0 + 16 * fm + 4 * lq + v;
+                sC[r * CS_STRIDE + col] = f32_to_bf16(val);
             }
+        }
     }
     __syncthreads();
     constexpr int CPR = BNm / 8;
@@ -1149,7 +1200,7 @@ __device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, bool 
 // allocation of the kernel's K loops.
 template <int BM, int NMAT, int ACT>
 __device__ __attribute__((noinline)) void pp_write_split(lds_char* lds, __amdgpu_buffer_rsrc_t rp, uint32_t wofs,
-                                                         int nsplit, bool rows_here, int row0, int wn, int l16,
+                                                         int nsplit, int nblk, int row0, int wn, int l16,
                                                          int lq, int tid, int rows, int n0, int N,
                                                          bf16_t* __restrict__ C_rows) {
     using S = PpShape<BM, NMAT>;
@@ -1161,7 +1212,7 @@ __device__ __attribute__((noinline)) void pp_write_split(lds_char* lds, __amdgpu
         for (int q = 1; q < nsplit; ++q) sum += load_part(rp, o + (uint32_t)q * SLOT_BYTES);
         return sum;
     };
-    pp_write_out<BM, NMAT, ACT>(lds, block, rows_here, row0, wn, l16, lq, tid, rows, n0, N, C_rows);
+    pp_write_out<BM, NMAT, ACT>(lds, block, nblk, row0, wn, l16, lq, tid, rows, n0, N, C_rows);
 }
 
 // All work items of one launch, ping-pong form.  part_buf / part_cnt as for gemm_tiles
@@ -1174,8 +1225,7 @@ __device__ __forceinline__ void gemm_tiles_pp(
     long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     using S = PpShape<BM, NMAT>;
     constexpr int BNm = S::BNm, GM = S::GM, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
-    constexpr int FM = S::FM, FN = S::FN, STAGE = S::STAGE, NSTAGE = S::NSTAGE, CS_STRIDE = S::CS_STRIDE;
-    constexpr int BROW = S::BROW, ADMA0 = S::ADMA0, ADMA1 = S::ADMA1, BDMA = S::BDMA;
+    constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
     static_assert(NMAT == 1 || FN % 2 == 0, "SwiGLU wavefronts hold gate and up halves");
     constexpr size_t SLOT = (size_t)BM * S::BN;       // floats per part slot
     static_assert(SLOT <= kGemmPartSlotFloats, "part slot larger than the workspace's");
@@ -1187,8 +1237,8 @@ __device__ __forceinline__ void gemm_tiles_pp(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wsub = (wave >> 1) & 1, wn = wave & 1;
+    const int wr = 2 * grp + wsub;                               // this wavefront's row quarter
     const int l16 = lane & 15, lq = lane >> 4;
-    const int row0 = grp * GM + wsub * WTM;                      // first tile row of this wavefront
 
     const int NT = (N + BNm - 1) / BNm;
     const int KT = (K + BK - 1) / BK;
@@ -1196,8 +1246,11 @@ __device__ __forceinline__ void gemm_tiles_pp(
     const int G = gridDim.x;
     const long long first = (long long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t rowB = (uint32_t)N * 2;
-    const int a_rd = (row0 + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
-    const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);
+    // A fragment reads at row 0 of the wavefront's rows (the rows move per item, by
+    // multiples of 16, which keep the A swizzle)
+    const int a_rd0 = l16 * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+    // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
+    const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
     const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
     // this wavefront's accumulators in a part slot (register layout, 16 bytes per lane per block)
     const uint32_t wofs = (uint32_t)((wave * FM * FN * 256 + lane * 4) * 4);
@@ -1218,7 +1271,14 @@ __device__ __forceinline__ void gemm_tiles_pp(
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
-        const bool rows_here = rows > row0;
+        // the tile's rows split evenly over the four row quarters, at a multiple of 16 (an
+        // expert with 256 rows in a 320-row tile multiplies 4 row blocks per wavefront,
+        // not 5, 5, 5 and 1)
+        const int rsplit = min(WTM, (rows + 63) / 64 * 16);
+        const int row0 = wr * rsplit;                            // first tile row of this wavefront
+        const int wrows = min(rows - row0, rsplit);
+        const int nblk = wrows > 0 ? (wrows + 15) / 16 : 0;
+        const int a_rd = a_rd0 + row0 * (BK * 2);
         int kt0 = 0, nsteps = KT;
         if constexpr (PART) {
             kt0 = __builtin_amdgcn_readfirstlane((int)((long long)part * KT / nsplit));
@@ -1238,10 +1298,10 @@ __device__ __forceinline__ void gemm_tiles_pp(
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         if (grp == 0)
-            pp_item<0, BM, NMAT, GATHER>(lds, kt0, nsteps, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
+            pp_item<0, BM, NMAT, GATHER>(lds, kt0, nsteps, nblk, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
                                          wave, lane, a_rd, b_rd, g, wn, acc);
         else
-            pp_item<1, BM, NMAT, GATHER>(lds, kt0, nsteps, rows_here, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
+            pp_item<1, BM, NMAT, GATHER>(lds, kt0, nsteps, nblk, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
                                          wave, lane, a_rd, b_rd, g, wn, acc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
         __syncthreads();
@@ -1253,7 +1313,7 @@ __device__ __forceinline__ void gemm_tiles_pp(
         if constexpr (PART) {
             rp = make_rsrc(pbuf + (size_t)slot * nsplit * SLOT, (uint32_t)(nsplit * SLOT * 4));
             wofs = (uint32_t)((wave * FM * FN * 256 + lane * 4) * 4);
-            if (rows_here) {
+            if (nblk > 0) {
                 const uint32_t pofs = (uint32_t)(part * SLOT * 4);
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
@@ -1265,10 +1325,10 @@ __device__ __forceinline__ void gemm_tiles_pp(
             if (!split_arrive(sp, flag)) return;
         }
         if constexpr (PART)
-            pp_write_split<BM, NMAT, ACT>(lds, rp, wofs, nsplit, rows_here, row0, wn, l16, lq, tid, rows, n0, N,
+            pp_write_split<BM, NMAT, ACT>(lds, rp, wofs, nsplit, nblk, row0, wn, l16, lq, tid, rows, n0, N,
                                           C + (long long)tl.row0 * N);
         else
-            pp_write_out<BM, NMAT, ACT>(lds, [&](int fm, int fn) { return acc[fm][fn]; }, rows_here, row0, wn, l16,
+            pp_write_out<BM, NMAT, ACT>(lds, [&](int fm, int fn) { return acc[fm][fn]; }, nblk, row0, wn, l16,
                                         lq, tid, rows, n0, N, C + (long long)tl.row0 * N);
     };
 
@@ -1294,26 +1354,21 @@ __device__ __forceinline__ void gemm_tiles_pp(
     }
 }
 
-template <int NMAT>
-constexpr size_t pp_lds_bytes() { return PpShape<256, NMAT>::LDS_BYTES; }
-
-// 256-row grouped GEMM, ping-pong form (512 threads).  It is launched together with the
-// 320-row kernel; whichever height the tile builder chose runs, the other returns.  (The
-// ping-pong form is faster where operands mostly hit in L2; on the weight stream from HBM
-// of 320-row tiles, whose reads come half a step later than in the 4-wavefront kernel,
-// it was slower.)  The SPLIT instance also splits the last round along K; the host
-// launches it only where K allows a split, since the split's code alone slows the
-// kernel's short-K items by about 2%.
-template <int NMAT, int ACT, bool GATHER, bool SPLIT>
+// Grouped GEMM for BM-row tiles (256 or 320), ping-pong form (512 threads).  The two
+// heights are launched together; whichever the tile builder chose runs, the other
+// returns.  The SPLIT instance also splits the last round along K; the host launches it
+// only where K allows a split, since the split's code alone slows the kernel's short-K
+// items by about 2%.
+template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm_pp(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
     long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
     extern __shared__ uint4 smem[];
-    if (__builtin_amdgcn_readfirstlane(ntiles_p[1]) != 256) return;
-    gemm_tiles_pp<256, NMAT, ACT, GATHER, SPLIT>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
-                                                 part_buf, part_cnt);
+    if (__builtin_amdgcn_readfirstlane(ntiles_p[1]) != BM) return;
+    gemm_tiles_pp<BM, NMAT, ACT, GATHER, SPLIT>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
+                                                part_buf, part_cnt);
 }
 
 // ------------------------------------------------------------------------ tile list
@@ -1437,16 +1492,22 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
     return hipSuccess;
 }
 
-// The ping-pong kernel of a launch pair (256-row tiles), split-capable or not.
-template <int NMAT, int ACT, bool GATHER, bool SPLIT>
+// 320-row tiles of a launch pair in the ping-pong kernel (else the 4-wavefront kernel).
+// Measured on the pages' worked shape (weights streamed from HBM), the ping-pong form
+// with the same rings and row split matched the 4-wavefront kernel on the first
+// projection and was 3% slower on the second, so the 4-wavefront kernel stays.
+constexpr bool kPp320 = false;
+
+// One ping-pong kernel of a launch pair (BM-row tiles), split-capable or not.
+template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
 static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
                          const void* B1, void* C, const Tile* tiles, const int32_t* ntiles,
                          long long max_items, int K, int N, const SplitBuffers& sb, hipStream_t st) {
     static bool ready = false;
     static int occ = 1;
     unsigned G = 0;
-    constexpr size_t pp_bytes = pp_lds_bytes<NMAT>();
-    auto kpp = k_grouped_gemm_pp<NMAT, ACT, GATHER, SPLIT>;
+    constexpr size_t pp_bytes = PpShape<BM, NMAT>::LDS_BYTES;
+    auto kpp = k_grouped_gemm_pp<BM, NMAT, ACT, GATHER, SPLIT>;
     hipError_t e = persistent_grid(kpp, pp_bytes, ready, occ, max_items, G, 512);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows, (const bf16_t*)B0,
@@ -1472,12 +1533,18 @@ static hipError_t run_gemm(const void* A, long long a_rows, const int32_t* gathe
         if constexpr (BM == 256 && BMB == 320) {
             // launch pair: 256-row tiles in the ping-pong kernel, 320-row tiles in the
             // 4-wavefront kernel; the one whose height was not chosen returns at once
-            hipError_t e = (!GATHER && sb.parts && (K + 31) / 32 >= 2 * kMinPartSteps)
-                               ? run_pp<NMAT, ACT, GATHER, !GATHER>(A, a_rows, gather_rows, B0, B1, C, tiles, ntiles,
-                                                                    max_items, K, N, sb, st)
-                               : run_pp<NMAT, ACT, GATHER, false>(A, a_rows, gather_rows, B0, B1, C, tiles, ntiles,
-                                                                  max_items, K, N, sb, st);
+            const bool split = !GATHER && sb.parts && (K + 31) / 32 >= 2 * kMinPartSteps;
+            hipError_t e = split ? run_pp<256, NMAT, ACT, GATHER, !GATHER>(A, a_rows, gather_rows, B0, B1, C, tiles,
+                                                                         ntiles, max_items, K, N, sb, st)
+                                 : run_pp<256, NMAT, ACT, GATHER, false>(A, a_rows, gather_rows, B0, B1, C, tiles,
+                                                                       ntiles, max_items, K, N, sb, st);
             if (e != hipSuccess) return e;
+            if constexpr (kPp320) {
+                return split ? run_pp<320, NMAT, ACT, GATHER, !GATHER>(A, a_rows, gather_rows, B0, B1, C, tiles,
+                                                                       ntiles, max_items, K, N, sb, st)
+                             : run_pp<320, NMAT, ACT, GATHER, false>(A, a_rows, gather_rows, B0, B1, C, tiles,
+                                                                     ntiles, max_items, K, N, sb, st);
+            }
             constexpr size_t lds_bytes = LdsShape<320, NMAT>::LDS_BYTES;
             auto kern = k_grouped_gemm_lds<320, 320, NMAT, ACT, GATHER>;
             e = persistent_grid(kern, lds_bytes, ready, occ, max_items, G);
