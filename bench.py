@@ -317,7 +317,10 @@ def _gemm_kernel_name(cfg, up: bool, counts) -> str:
         return "k_grouped_gemm_lds<128, 128, %d, %d, %s>" % (nmat, act, gather)
     if _tile_height(cfg, counts) == 320:
         return "k_grouped_gemm_lds<320, 320, %d, %d, %s>" % (nmat, act, gather)
-    return "k_grouped_gemm_pp<%d, %d, %s>" % (nmat, act, gather)
+    # the second projection runs the split-capable instance where K = F allows two parts
+    # of 64 K steps of 32
+    split = "true" if (not up and (cfg.F + 31) // 32 >= 128) else "false"
+    return "k_grouped_gemm_pp<256, %d, %d, %s, %s>" % (nmat, act, gather, split)
 
 
 def _roofline(kd, peak_flops):
