@@ -873,8 +873,8 @@ __device__ __forceinline__ void gemm_tiles(
             const int r = c / CPR, cc = c % CPR;
             const int col = n0 + cc * 8;
             if (col < N)
-                *reinterpret_cast<uint4*>(C + (long long)(tl.row0 + r) * N + col) =
-                    *reinterpret_cast<const uint4*>(sC + r * CS_STRIDE + cc * 8);
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * CS_STRIDE + cc * 8),
+                                            reinterpret_cast<u32x4_t*>(C + (long long)(tl.row0 + r) * N + col));
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // stores out before the next DMA count
         __syncthreads();
@@ -1197,8 +1197,9 @@ __device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, int n
         const int r = c / CPR, cc = c % CPR;
         const int col = n0 + cc * 8;
         if (col < N)
-            *reinterpret_cast<u32x4_t*>(C_rows + (long long)r * N + col) =
-                *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sC + r * CS_STRIDE + cc * 8);
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sC + r * CS_STRIDE + cc * 8),
+                reinterpret_cast<u32x4_t*>(C_rows + (long long)r * N + col));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
