@@ -65,7 +65,7 @@ Layout layout_of(const moe_shape& s) {
     const size_t NS = (P + kSeg - 1) / kSeg;
     Layout L{};
     size_t o = 0;
-    L.logits = o;       o += up((size_t)gate_splits(s.T, s.H, s.E) * s.T * s.E * 4);
+    L.logits = o;       o += up((size_t)gate_splits(s.T, s.H, s.E, s.dtype) * s.T * s.E * 4);
     L.topk_idx = o;     o += up(P * 4);
     L.topk_w = o;       o += up(P * 4);
     L.counts = o;       o += up((size_t)s.E * 4);
@@ -309,7 +309,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     int32_t* offsets = at<int32_t>(workspace, L.offsets);
     int32_t* sorted_token = at<int32_t>(workspace, L.sorted_token);
     int32_t* row_of_pair = at<int32_t>(workspace, L.row_of_pair);
-    const int splits = gate_splits(s.T, s.H, s.E);
+    const int splits = gate_splits(s.T, s.H, s.E, s.dtype);
     if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[0], stream), "stage event");
     HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, stream), "gate_logits");
     HIPCHK(launch_topk(logits, splits, nullptr, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");

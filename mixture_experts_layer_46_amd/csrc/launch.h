@@ -40,7 +40,7 @@ enum GemmCfg { GEMM_M16 = 0, GEMM_M64 = 1, GEMM_M128 = 2, GEMM_M256 = 3 };
 void gemm_cfg_heights(GemmCfg c, int* bma, int* bmb);
 
 // K splits of the gate projection (partial sums [splits][T][E]) for a layer shape
-int gate_splits(long long T, int H, int E);
+int gate_splits(long long T, int H, int E, int dtype);   // split-K ranges of the gate projection
 hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out,
                               long long T, int H, int E, int splits, hipStream_t st);
 // top-k over the sum of `nparts` partial logits; the sum goes to logits_out if not NULL

@@ -6,8 +6,10 @@
 //
 // logits = x @ W_g in fp32 ([FourStage §2.1]; [Principles §2.4]: the gate stays fp32 so
 // near-equal logits are ranked the same way).  The projection is a thin GEMM
-// ([T, H] x [H, E], E <= 256) run on the fp32 MFMA (v_mfma_f32_16x16x4_f32): exact
-// widening of bf16 x, fp32 products and accumulation.  Top-k is one wavefront per
+// ([T, H] x [H, E], E <= 256).  For fp32 x, and for short batches, it runs on the fp32
+// MFMA (v_mfma_f32_16x16x4_f32): exact widening of bf16 x, fp32 products and
+// accumulation.  For bf16 x it runs on the bf16 MFMA with the weights split exactly
+// into three bf16 parts (k_gate_logits_x3): the same fp32 products and accumulation.  Top-k is one wavefront per
 // token: each lane holds up to four experts, k rounds of a wave-wide arg-max pick
 // the winners ([FourStage §2.2]); gates are the softmax over the chosen logits,
 // which equals the full softmax renormalised over the k chosen ([Principles §2.2]).
@@ -119,6 +121,133 @@ __global__ __launch_bounds__(256) void k_gate_logits(const XT* __restrict__ x,
         }
     }
     // 16x16 fp32 block: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
+    float* o = out + (size_t)blockIdx.z * T * E;
+    const int e = e0 + wave * 16 + (lane & 15);
+    if (e < E) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = m0 + fm * 16 + 4 * (lane >> 4) + v;
+                if (t < T) o[(size_t)t * E + e] = acc[fm][v];
+            }
+    }
+}
+
+// Gate projection for bf16 x on the bf16 MFMA.  Each fp32 gate weight is split exactly
+// into three bf16 parts, w = w1 + w2 + w3 (w1 = bf16(w), w2 = bf16(w - w1), w3 =
+// bf16(w - w1 - w2); each difference is exact, and 3 x 8 significant bits cover fp32's
+// 24).  A bf16 x times a bf16 part is exact in fp32, so x . w = x . w3 + x . w2 + x . w1
+// runs as three v_mfma_f32_16x16x32_bf16 with fp32 accumulation: the same fp32
+// products and accumulation as the fp32 MFMA, at 3 x 16 instead of 8 x 32 cycles per
+// 32 of K.  (Gate weights below 2^-110 or so would lose low bits in the third part.)
+// Tile: TM tokens x 64 experts per workgroup, K in steps of 64 over this workgroup's K
+// range (split-K as in k_gate_logits).  Wave w owns expert columns [16w, 16w + 16).
+// x stays row-major in LDS, the split weights are stored expert-major (k contiguous), so
+// both MFMA operands are single 16-byte LDS reads.
+__device__ __forceinline__ void split3_bf16(float w, float& h, float& m, float& l) {
+    h = (float)(__bf16)w;
+    const float r = w - h;
+    m = (float)(__bf16)r;
+    l = r - m;                   // exactly representable in bf16
+}
+
+constexpr int GX_PITCH = GT_K + 8;          // bf16 per LDS row (16-byte pad)
+
+template <int TM>
+__global__ __launch_bounds__(256) void k_gate_logits_x3(const bf16_t* __restrict__ x,
+                                                        const float* __restrict__ wg,
+                                                        float* __restrict__ out, int T, int H, int E,
+                                                        int kchunk) {
+    __shared__ __attribute__((aligned(16))) bf16_t sX[TM][GX_PITCH];
+    __shared__ __attribute__((aligned(16))) bf16_t sW[3][GT_E][GX_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m0 = blockIdx.x * TM, e0 = blockIdx.y * GT_E;
+    const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
+    constexpr int FM = TM / 16;
+    // x loader: TM rows x 8 chunks of 8 bf16 per step; thread -> (row, XCH chunks)
+    constexpr int XCH = TM * 8 / 256 > 0 ? TM * 8 / 256 : 1;
+    constexpr bool XPART = TM * 8 < 256;
+    const int xrow = tid / (8 / XCH), xc0 = (tid % (8 / XCH)) * XCH;
+    // W loader: thread -> k rows 4 kq .. 4 kq + 3, experts 4 eg .. 4 eg + 3
+    const int kq = tid & 15, eg = tid >> 4;
+    uint4 xr[XCH];
+    float4 wr[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int t = m0 + xrow, kk = k0 + 8 * (xc0 + j);
+            xr[j] = make_uint4(0u, 0u, 0u, 0u);
+            if ((!XPART || tid < TM * 8) && t < T && kk < kend)
+                xr[j] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = k0 + 4 * kq + j, e = e0 + 4 * eg;
+            wr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kk < kend) {
+                if (e + 3 < E) {
+                    wr[j] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
+                } else {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = (e + i < E) ? wg[(size_t)kk * E + e + i] : 0.f;
+                    wr[j] = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    };
+    auto lstore = [&]() {
+        if (!XPART || tid < TM * 8) {
+#pragma unroll
+            for (int j = 0; j < XCH; ++j) *reinterpret_cast<uint4*>(&sX[xrow][8 * (xc0 + j)]) = xr[j];
+        }
+        // expert i of this thread: its 4 k values, split into the three bf16 planes
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float w4[4] = {i == 0 ? wr[0].x : i == 1 ? wr[0].y : i == 2 ? wr[0].z : wr[0].w,
+                                 i == 0 ? wr[1].x : i == 1 ? wr[1].y : i == 2 ? wr[1].z : wr[1].w,
+                                 i == 0 ? wr[2].x : i == 1 ? wr[2].y : i == 2 ? wr[2].z : wr[2].w,
+                                 i == 0 ? wr[3].x : i == 1 ? wr[3].y : i == 2 ? wr[3].z : wr[3].w};
+            float h[4], m[4], l[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split3_bf16(w4[j], h[j], m[j], l[j]);
+            const int e = 4 * eg + i;
+            *reinterpret_cast<uint2*>(&sW[0][e][4 * kq]) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            *reinterpret_cast<uint2*>(&sW[1][e][4 * kq]) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
+            *reinterpret_cast<uint2*>(&sW[2][e][4 * kq]) = make_uint2(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]));
+        }
+    };
+    f32x4_t acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int fr = lane & 15, fq = lane >> 4;
+    if (kbeg < kend) {
+        gload(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (k0 + GT_K < kend) gload(k0 + GT_K);
+#pragma unroll
+            for (int ks = 0; ks < GT_K; ks += 32) {
+                bf16x8_t b[3];
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[p] = *reinterpret_cast<const bf16x8_t*>(&sW[p][16 * wave + fr][ks + 8 * fq]);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sX[16 * fm + fr][ks + 8 * fq]);
+                    // the small parts first
+                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], acc[fm], 0, 0, 0);
+                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[fm], 0, 0, 0);
+                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[fm], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // 16x16 block: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
     float* o = out + (size_t)blockIdx.z * T * E;
     const int e = e0 + wave * 16 + (lane & 15);
     if (e < E) {
@@ -255,9 +384,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 // -------------------------------------------------------------------- launchers
-int gate_splits(long long T, int H, int E) {
+// Row-tile height of the gate projection: 16 tokens for short batches (fp32 MFMA), else
+// 128 for bf16 x (split weights, whose conversion each workgroup repeats: taller tiles
+// amortise it) and 64 for fp32 x.
+int gate_tile_rows(long long T, int dtype) { return T <= 256 ? 16 : (dtype == MOE_F32 ? 64 : 128); }
+
+int gate_splits(long long T, int H, int E, int dtype) {
     if (T <= 0) return 1;
-    const long long tm = T <= 256 ? 16 : 64;
+    const long long tm = gate_tile_rows(T, dtype);
     const long long base = ((T + tm - 1) / tm) * ((E + GT_E - 1) / GT_E);
     long long sp = (512 + base - 1) / base;
     const long long maxs = (H + 255) / 256;
@@ -276,12 +410,12 @@ hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* 
             hipLaunchKernelGGL((k_gate_logits<16, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
         else
             hipLaunchKernelGGL((k_gate_logits<16, bf16_t>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
-    } else {
+    } else if (dtype == MOE_F32) {
         const dim3 grid((unsigned)((T + 63) / 64), gy, (unsigned)splits);
-        if (dtype == MOE_F32)
-            hipLaunchKernelGGL((k_gate_logits<64, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
-        else
-            hipLaunchKernelGGL((k_gate_logits<64, bf16_t>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
+        hipLaunchKernelGGL((k_gate_logits<64, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
+    } else {
+        const dim3 grid((unsigned)((T + 127) / 128), gy, (unsigned)splits);
+        hipLaunchKernelGGL((k_gate_logits_x3<128>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
     }
     return hipGetLastError();
 }
