@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void k_gate_logits(const XT* __restrict__ x,
 // 24).  A bf16 x times a bf16 part is exact in fp32, so x . w = x . w3 + x . w2 + x . w1
 // runs as three v_mfma_f32_16x16x32_bf16 with fp32 accumulation: the same fp32
 // products and accumulation as the fp32 MFMA, at 3 x 16 instead of 8 x 32 cycles per
-// 32 of K.  (Gate weights below 2^-110 or so would lose low bits in the third part.)
+// 32 of K.  (Outside the exact range: weights above about 3.39e38, whose bf16 rounding
+// is infinite, and below about 2^-110, whose third part loses low bits.)
 // Tile: TM tokens x 64 experts per workgroup, K in steps of 64 over this workgroup's K
 // range (split-K as in k_gate_logits).  Wave w owns expert columns [16w, 16w + 16).
 // x stays row-major in LDS, the split weights are stored expert-major (k contiguous), so

@@ -56,9 +56,15 @@ def test_route_from_logits_bit_exact(lib, T, E, k, use_bias, flags):
     np.testing.assert_allclose(w.cpu().numpy(), rg, rtol=1e-6, atol=1e-7)
 
 
+# T > 256 with bf16 x takes the split-weight bf16 MFMA gate (128-token tiles); ragged
+# K (H = 200), several expert tiles (E = 256) and a ragged expert count (E = 37)
+ROUTE_X_CASES = [(333, 200, 64, 2), (1000, 4096, 256, 8), (700, 64, 37, 3), (200, 512, 64, 2)]
+
+
+@pytest.mark.parametrize("T,H,E,k", ROUTE_X_CASES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_route_from_x(lib, dtype):
-    cfg = MoEConfig("r", T=333, H=200, E=64, k=2, F=8, ffn="swiglu", dtype=dtype, bias="normal0.5")
+def test_route_from_x(lib, dtype, T, H, E, k):
+    cfg = MoEConfig("r", T=T, H=H, E=E, k=k, F=8, ffn="swiglu", dtype=dtype, bias="normal0.5")
     say(f"route_from_x {cfg}")
     d = generate(cfg, experts=False)
     x, wg, b = d["x"].cuda(), d["w_gate"].cuda(), d["bias"].cuda()
@@ -69,7 +75,7 @@ def test_route_from_x(lib, dtype):
     assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
     scores, ridx, rg = O.route(to_numpy(d["x"]), to_numpy(d["w_gate"]), to_numpy(d["bias"]), cfg.k)
     flips = check_selection(idx.cpu().numpy(), scores, cfg.k)
-    assert len(flips) <= 2
+    assert len(flips) <= max(2, cfg.T // 200)
     same = np.setdiff1d(np.arange(cfg.T), list(flips))
     np.testing.assert_allclose(w.cpu().numpy()[same], rg[same], rtol=2e-5, atol=1e-6)
 
