@@ -173,40 +173,45 @@ __global__ __launch_bounds__(256) void k_gate_logits_x3(const bf16_t* __restrict
     const int xrow = tid / (8 / XCH), xc0 = (tid % (8 / XCH)) * XCH;
     // W loader: thread -> k rows 4 kq .. 4 kq + 3, experts 4 eg .. 4 eg + 3
     const int kq = tid & 15, eg = tid >> 4;
-    uint4 xr[XCH];
-    float4 wr[4];
-    auto gload = [&](int k0) {
+    // one K step's operands in registers; two are in flight (the loads of step k + 2 are
+    // issued before step k's MFMAs), which covers HBM latency for x
+    struct Stage {
+        uint4 xr[XCH];
+        float4 wr[4];
+    };
+    auto gload = [&](Stage& sg, int k0) {
 #pragma unroll
         for (int j = 0; j < XCH; ++j) {
             const int t = m0 + xrow, kk = k0 + 8 * (xc0 + j);
-            xr[j] = make_uint4(0u, 0u, 0u, 0u);
+            sg.xr[j] = make_uint4(0u, 0u, 0u, 0u);
             if ((!XPART || tid < TM * 8) && t < T && kk < kend)
-                xr[j] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+                sg.xr[j] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kk = k0 + 4 * kq + j, e = e0 + 4 * eg;
-            wr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            sg.wr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (kk < kend) {
                 if (e + 3 < E) {
-                    wr[j] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
+                    sg.wr[j] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
                 } else {
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = (e + i < E) ? wg[(size_t)kk * E + e + i] : 0.f;
-                    wr[j] = make_float4(v[0], v[1], v[2], v[3]);
+                    sg.wr[j] = make_float4(v[0], v[1], v[2], v[3]);
                 }
             }
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](const Stage& sg) {
         if (!XPART || tid < TM * 8) {
 #pragma unroll
-            for (int j = 0; j < XCH; ++j) *reinterpret_cast<uint4*>(&sX[xrow][8 * (xc0 + j)]) = xr[j];
+            for (int j = 0; j < XCH; ++j) *reinterpret_cast<uint4*>(&sX[xrow][8 * (xc0 + j)]) = sg.xr[j];
         }
         // expert i of this thread: its 4 k values, split into the three bf16 planes
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const float4* wr = sg.wr;
             const float w4[4] = {i == 0 ? wr[0].x : i == 1 ? wr[0].y : i == 2 ? wr[0].z : wr[0].w,
                                  i == 0 ? wr[1].x : i == 1 ? wr[1].y : i == 2 ? wr[1].z : wr[1].w,
                                  i == 0 ? wr[2].x : i == 1 ? wr[2].y : i == 2 ? wr[2].z : wr[2].w,
@@ -224,28 +229,39 @@ __global__ __launch_bounds__(256) void k_gate_logits_x3(const bf16_t* __restrict
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int fr = lane & 15, fq = lane >> 4;
-    if (kbeg < kend) {
-        gload(kbeg);
-        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
-            __syncthreads();
-            lstore();
-            __syncthreads();
-            if (k0 + GT_K < kend) gload(k0 + GT_K);
+    auto mfma_step = [&]() {
 #pragma unroll
-            for (int ks = 0; ks < GT_K; ks += 32) {
-                bf16x8_t b[3];
+        for (int ks = 0; ks < GT_K; ks += 32) {
+            bf16x8_t b[3];
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    b[p] = *reinterpret_cast<const bf16x8_t*>(&sW[p][16 * wave + fr][ks + 8 * fq]);
+            for (int p = 0; p < 3; ++p)
+                b[p] = *reinterpret_cast<const bf16x8_t*>(&sW[p][16 * wave + fr][ks + 8 * fq]);
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sX[16 * fm + fr][ks + 8 * fq]);
-                    // the small parts first
-                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], acc[fm], 0, 0, 0);
-                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[fm], 0, 0, 0);
-                    acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[fm], 0, 0, 0);
-                }
+            for (int fm = 0; fm < FM; ++fm) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sX[16 * fm + fr][ks + 8 * fq]);
+                // the small parts first
+                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], acc[fm], 0, 0, 0);
+                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[fm], 0, 0, 0);
+                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[fm], 0, 0, 0);
             }
+        }
+    };
+    if (kbeg < kend) {
+        Stage s0, s1;
+        gload(s0, kbeg);
+        gload(s1, kbeg + GT_K);                 // (past kend: zeros, no loads)
+        for (int k0 = kbeg; k0 < kend; k0 += 2 * GT_K) {
+            __syncthreads();
+            lstore(s0);
+            __syncthreads();
+            gload(s0, k0 + 2 * GT_K);
+            mfma_step();
+            if (k0 + GT_K >= kend) break;
+            __syncthreads();
+            lstore(s1);
+            __syncthreads();
+            gload(s1, k0 + 3 * GT_K);
+            mfma_step();
         }
     }
     // 16x16 block: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
