@@ -55,10 +55,18 @@ __global__ __launch_bounds__(256) void k_seg_scan(int32_t* __restrict__ segcnt, 
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (long long s = 0; s < NS; ++s) {
-            const int c = segcnt[s * E + e];
-            segcnt[s * E + e] = run;
-            run += c;
+        // segments in batches of 16: the batch's loads are issued together, so the chain
+        // of dependent loads and stores no longer costs one memory latency per segment
+        constexpr int B = 16;
+        for (long long s0 = 0; s0 < NS; s0 += B) {
+            int c[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) c[j] = s0 + j < NS ? segcnt[(s0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (s0 + j < NS) segcnt[(s0 + j) * E + e] = run;
+                run += c[j];
+            }
         }
         counts[e] = run;
     }
