@@ -437,6 +437,43 @@ __device__ __forceinline__ void dma_step(lds_char* lds, __amdgpu_buffer_rsrc_t r
     dma_w<BM, NMAT>(lds + S::W_RING + (rw_step % S::NW) * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
 }
 
+// Instruction I of one step's DMA (I < ADMA: A instruction I, else W instruction
+// I - ADMA), with the targets of dma_step; lets the 320-row K step spread its DMA
+// issues between its MFMAs.
+template <int BM, int NMAT, int I>
+__device__ __forceinline__ void dma_one(lds_char* lds, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
+                                        __amdgpu_buffer_rsrc_t rb1,
+                                        const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl,
+                                        int kt0, int r, int K, uint32_t rowB, int wave) {
+    using S = LdsShape<BM, NMAT>;
+    if constexpr (I < S::ADMA) {
+        const int step = r + S::NA - 1;
+        const uint32_t k0 = (uint32_t)(kt0 + step) * S::BK;
+        lds_char* dst = lds + (step % S::NA) * S::A_STAGE + (wave * S::ADMA + I) * 1024;
+        const uint32_t off = (k0 + pl.a_k[I] < (uint32_t)K) ? pl.a_off[I] + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)dst, 16, off, 0, 0, 0);
+    } else {
+        constexpr int i = I - S::ADMA;
+        const int step = r + S::NW - 1;
+        const uint32_t k0 = (uint32_t)(kt0 + step) * S::BK;
+        const int j = wave * S::BDMA + i;
+        lds_char* dst = lds + S::W_RING + (step % S::NW) * S::B_STAGE + j * 1024;
+        const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
+        constexpr int per_mat = S::BMAT_DMA;
+        const __amdgpu_buffer_rsrc_t rb = (NMAT == 2 && j >= per_mat) ? rb1 : rb0;
+        constexpr int aux = S::W_AUX;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)dst, 16, off, 0, 0, aux);
+    }
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 // The DMA ahead of a work's first step, issued as the steps -(NW - 1) .. -1 would have
 // issued it, so that the first steps wait with the same count as the rest: A of steps
 // below 0 is a zero-loading placeholder.
@@ -502,15 +539,32 @@ __device__ __attribute__((always_inline)) inline void kstep(
 #pragma unroll
     for (int fm = 1; fm < FM; ++fm) read_a(fm);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (BM == 320) {
+        // one DMA instruction after each 16-row block's MFMAs (the rest after the last), in
+        // an order the scheduler keeps: a burst of DMA issues could stall the wavefront on
+        // the texture-address queue while the MFMA pipe has nothing queued
+        constexpr int D = S::DPW;
+        static_for<0, FM>([&](auto fmc) {
+            constexpr int fm = decltype(fmc)::value;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            if constexpr (fm < D) dma_one<BM, NMAT, fm>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<FM, D>([&](auto ic) {
+            dma_one<BM, NMAT, decltype(ic)::value>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
+        });
+        return;
+    }
     dma_step<BM, NMAT>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-    // issue order: one DMA instruction, then FM*FN/DPW MFMAs, DPW times (not for the
-    // 320-row tile, whose 60 MFMAs and 9 DMA instructions do not pair evenly; there the
-    // pattern made the register allocator move accumulators every step)
+    // issue order: one DMA instruction, then FM*FN/DPW MFMAs, DPW times (the 320-row tile
+    // interleaves by hand above: this pattern made the allocator move its accumulators)
     if constexpr (BM != 320) {
         constexpr int PER = FM * FN / S::DPW > 0 ? FM * FN / S::DPW : 1;
 #pragma unroll
