@@ -1159,11 +1159,12 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
     bf16x8_t af[FM], bfr[FN];
     if constexpr (GROUP == 1) kloop_barrier();                  // group 1's idle first phase
     for (int kt = 0; kt < KT; ++kt) {
-        // read phase: DMA of the steps NA - 1 and NW - 1 ahead, fragments of step kt
-        pp_dma_step<BM, NMAT, GROUP>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
+        // read phase: fragments of step kt, then the DMA of the steps NA - 1 and NW - 1 ahead
         // (read by every wavefront: a branch here makes the compiler copy the fragments)
         pp_read<BM, NMAT>(lds + (kt % S::NA) * S::A_STAGE, lds + S::W_RING + (kt % S::NW) * S::B_STAGE, a_rd, b_rd,
                           g, wn, af, bfr);
+        __builtin_amdgcn_sched_barrier(0);
+        pp_dma_step<BM, NMAT, GROUP>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (GROUP == 1) wait_vmcnt<VMCNT>();           // step kt + 1 complete
         kloop_barrier();
