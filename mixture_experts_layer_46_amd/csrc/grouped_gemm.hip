@@ -595,6 +595,82 @@ __device__ __attribute__((always_inline)) inline void kloop(
     }
 }
 
+// The 320-row K loop with the barrier of step r + 1 moved before the last 16-row block
+// of step r: every wavefront has then read all of step r's fragments (lgkmcnt(0)) and
+// issued step r's DMA, so the barrier means what it meant at the top of step r + 1.
+// Step r + 1's first A block and B fragments are read right after it, while step r's
+// last block of MFMAs runs, so the next step's MFMAs do not start behind a barrier
+// and an LDS round trip.  Barriers per item: KT + 1 (one more than kloop; the DMA-only
+// wavefronts of a 320-row tile add it after their loop).
+template <int BM, int NMAT, int FMA>
+__device__ __attribute__((always_inline)) inline void kloop_early(
+    lds_char* lds, int KT, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
+    const DmaPlan<LdsShape<BM, NMAT>::ADMA, LdsShape<BM, NMAT>::BDMA>& pl, int K, uint32_t rowB, int wave,
+    int a_rd, int b_rd, int g, int wn, f32x4_t (&acc)[FMA][LdsShape<BM, NMAT>::FN], int kt0) {
+    using S = LdsShape<BM, NMAT>;
+    constexpr int FM = FMA, FN = S::FN, BROW = S::BROW, D = S::DPW;
+    auto a_stage = [&](int r) -> const lds_char* { return lds + (r % S::NA) * S::A_STAGE; };
+    auto b_stage = [&](int r) -> const lds_char* { return lds + S::W_RING + (r % S::NW) * S::B_STAGE; };
+    auto read_a = [&](const lds_char* As, int fm) -> bf16x8_t {
+        return *(const __attribute__((address_space(3))) bf16x8_t*)(As + a_rd + fm * 16 * S::BK * 2);
+    };
+    auto read_b = [&](const lds_char* Bs, int fn) -> bf16x8_t {
+        int mat, blk;
+        if constexpr (NMAT == 1) {
+            mat = 0;
+            blk = wn * (S::WTN / 16) + fn;
+        } else {
+            mat = fn < FN / 2 ? 0 : 1;
+            blk = wn * (FN / 2) + (fn % (FN / 2));
+        }
+        const lds_char* p = Bs + mat * S::BK * BROW + b_rd + (wblk<BM, NMAT>(blk, g) << 5);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
+    // a0 and bf: step r's first A block and B fragments, read while step r - 1 finished
+    bf16x8_t a0, bf[FN];
+    wait_vmcnt<S::VMCNT>();
+    kloop_barrier();
+    a0 = read_a(a_stage(0), 0);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) bf[fn] = read_b(b_stage(0), fn);
+    for (int r = 0; r < KT; ++r) {
+        bf16x8_t af[FM];
+        af[0] = a0;
+#pragma unroll
+        for (int fm = 1; fm < FM; ++fm) af[fm] = read_a(a_stage(r), fm);
+        __builtin_amdgcn_sched_barrier(0);
+        // blocks 0 .. FM - 2, one DMA instruction after each block's first MFMA
+        static_for<0, FM - 1>([&](auto fmc) {
+            constexpr int fm = decltype(fmc)::value;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+            if constexpr (fm < D) dma_one<BM, NMAT, fm>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<FM - 1, D>([&](auto ic) {
+            dma_one<BM, NMAT, decltype(ic)::value>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
+        });
+        // the barrier of step r + 1, also after the last step (the reads then take stages
+        // nobody uses: no branch here, which would make the compiler copy the accumulators)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<S::VMCNT>();
+        kloop_barrier();
+        a0 = read_a(a_stage(r + 1), 0);
+        // the last block: each B fragment is re-read for step r + 1 once its MFMA has taken it
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            acc[FM - 1][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[FM - 1], bf[fn], acc[FM - 1][fn], 0, 0, 0);
+            bf[fn] = read_b(b_stage(r + 1), fn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Workgroup barrier of the K loop.  Each wavefront has already waited for its own DMA
 // of the step (wait_vmcnt) and its fragment reads of the previous step were consumed by
 // MFMAs before it arrives, so the barrier alone makes the stage complete for all and the
@@ -704,7 +780,8 @@ __device__ __attribute__((always_inline)) inline bool rows_item(
     for (int i = 0; i < FMA; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc_zero(acc[i][j]);
-    kloop<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc, kt0);
+    if constexpr (BM == 320) kloop_early<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc, kt0);
+    else kloop<BM, NMAT, FMA>(lds, KT, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc, kt0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
     __syncthreads();
     const int lane = threadIdx.x & 63;
@@ -916,6 +993,10 @@ __device__ __forceinline__ void gemm_tiles(
                 wait_vmcnt<S::VMCNT>();
                 kloop_barrier();
                 dma_step<BM, NMAT>(lds, ra, rb0, rb1, pl, kt0, r, K, rowB, wave);
+            }
+            if constexpr (BM == 320) {      // the last barrier of kloop_early
+                wait_vmcnt<S::VMCNT>();
+                kloop_barrier();
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
