@@ -77,7 +77,7 @@ Layout layout_of(const moe_shape& s) {
     L.ntiles = o;       o += up(4);
     // the bf16 grouped GEMM's split of the last round: part slots and their counters
     const bool split = s.dtype == MOE_BF16 && pick_cfg(s) != GEMM_M16;
-    L.part_cnt = o;     o += split ? up((size_t)kGemmPartSlots * 4) : 0;
+    L.part_cnt = o;     o += split ? up((size_t)(kGemmPartSlots + kGemmQueues) * 4) : 0;
     L.parts = o;        o += split ? up((size_t)kGemmPartSlots * kGemmPartSlotFloats * 4) : 0;
     L.h = o;            o += up(P * s.F * es);
     L.y = o;            o += up(P * s.H * es);
@@ -160,8 +160,9 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     const GemmCfg cfg = pick_cfg(s);
     int bma, bmb;
     gemm_cfg_heights(cfg, &bma, &bmb);
-    SplitBuffers sb{nullptr, nullptr};
-    if (cfg != GEMM_M16) sb = SplitBuffers{at<float>(ws, L.parts), at<int>(ws, L.part_cnt)};
+    SplitBuffers sb{nullptr, nullptr, nullptr};
+    if (cfg != GEMM_M16)
+        sb = SplitBuffers{at<float>(ws, L.parts), at<int>(ws, L.part_cnt), at<int>(ws, L.part_cnt) + kGemmPartSlots};
     HIPCHK(launch_build_tiles_for(offsets, s.E, cfg, s.H, s.F, swiglu, tiles, ntiles, sb.counts, st), "build_tiles");
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
                                    ntiles, max_tiles_for(P, s.E, std::min(bma, bmb)), cfg, s.H, s.F, swiglu, sb, ev, st),

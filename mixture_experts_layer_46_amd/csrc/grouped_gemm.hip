@@ -1368,7 +1368,7 @@ __device__ __forceinline__ void gemm_tiles_pp(
     uint4* smem, const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt, int* __restrict__ item_q) {
     using S = PpShape<BM, NMAT>;
     constexpr int BNm = S::BNm, GM = S::GM, WTM = S::WTM, WTN = S::WTN, BK = S::BK;
     constexpr int FM = S::FM, FN = S::FN, BROW = S::BROW;
@@ -1484,13 +1484,28 @@ __device__ __forceinline__ void gemm_tiles_pp(
         const WorkSplit wsp(total, G, pbuf ? KT : 0);
         main_end = wsp.split == 1 ? total : wsp.full;
     }
-    long long w = first;
-    for (; w < main_end; w += G) run_item(w, 0, 1, -1, std::false_type{});
+    // Work order.  The static order gives workgroup b the work indices first, first + G, ...
+    // (XCD b % 8 runs a contiguous chunk of G / 8 indices per round).  With item_q, the
+    // workgroups of an XCD instead take that XCD's indices in order from a counter, so the
+    // items running together on an XCD stay a contiguous window of the order (the row
+    // tiles and weight slices they share stay shared) even when items differ in length.
+    const int xcd = blockIdx.x & 7, per_xcd = G >> 3;
+    int* const q = item_q ? item_q + xcd : nullptr;
+    int* const fetch_word = flag + 1;
+    auto fetch = [&]() -> long long {
+        if (tid == 0) *fetch_word = atomicAdd(q, 1);
+        __syncthreads();
+        const int c = *fetch_word;
+        __syncthreads();
+        return (long long)(c / per_xcd) * G + (long long)xcd * per_xcd + c % per_xcd;
+    };
+    long long w = q ? fetch() : first;
+    for (; w < main_end; w = q ? fetch() : w + G) run_item(w, 0, 1, -1, std::false_type{});
     if constexpr (SPLIT) {
         // the split is derived again from the tile count (reloaded after the loop's memory
         // clobbers), so that none of it is held through the full rounds
         const WorkSplit wsp((long long)(*ntiles_p) * NT, G, pbuf ? KT : 0);
-        for (; w < wsp.nwork; w += G) {
+        for (; w < wsp.nwork; w = q ? fetch() : w + G) {
             long long item;
             int part, slot;
             wsp.item_of(w, item, part, slot);
@@ -1510,11 +1525,11 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_pp(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C,
     const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles_p, int K, int N,
-    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt) {
+    long long a_rows, float* __restrict__ part_buf, int* __restrict__ part_cnt, int* __restrict__ item_q) {
     extern __shared__ uint4 smem[];
     if (__builtin_amdgcn_readfirstlane(ntiles_p[1]) != BM) return;
     gemm_tiles_pp<BM, NMAT, ACT, GATHER, SPLIT>(smem, A, gather_rows, B0, B1, C, tiles, ntiles_p, K, N, a_rows,
-                                                part_buf, part_cnt);
+                                                part_buf, part_cnt, item_q);
 }
 
 // ------------------------------------------------------------------------ tile list
@@ -1531,6 +1546,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
     // the grouped GEMMs' split-part counters start at zero (each launch leaves them so)
     static_assert(kPartSlots <= 256, "one counter per thread");
     if (part_cnt && threadIdx.x < kPartSlots) part_cnt[threadIdx.x] = 0;
+    if (part_cnt && threadIdx.x < kGemmQueues) part_cnt[kPartSlots + threadIdx.x] = 0;   // the fetch counters
     __shared__ int buf[2][256];
     __shared__ long long cost[2][4];
     const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
@@ -1644,6 +1660,12 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
 // projection and was 3% slower on the second, so the 4-wavefront kernel stays.
 constexpr bool kPp320 = false;
 
+// The ordered per-XCD fetch costs an atomic and two barriers per item, which items of
+// under 128 K steps (4096 of K) do not earn back: they keep the static order.  On the
+// fine-grained skewed shape the fetch took the first projection (224 steps) from 4.58
+// to 4.38 ms, and made the second (64 steps) 1.3% slower.
+constexpr int kFetchMinSteps = 128;
+
 // One ping-pong kernel of a launch pair (BM-row tiles), split-capable or not.
 template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
 static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
@@ -1657,7 +1679,8 @@ static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_
     hipError_t e = persistent_grid(kpp, pp_bytes, ready, occ, max_items, G, 512);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows, (const bf16_t*)B0,
-                       (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows, sb.parts, sb.counts);
+                       (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows, sb.parts, sb.counts,
+                       (G % 8 == 0 && (K + 31) / 32 >= kFetchMinSteps) ? sb.queue : nullptr);
     return hipGetLastError();
 }
 
@@ -1731,7 +1754,9 @@ static hipError_t run_ffn(const void* a, long long a_rows, const int32_t* gather
     }
     if (e != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-    e = run_gemm<BM, BMB, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items, F, H, sb, st);
+    SplitBuffers sb2 = sb;             // the second projection's own fetch counters
+    if (sb2.queue) sb2.queue += 8;
+    e = run_gemm<BM, BMB, 1, WAVES_M, 0, false>(h, 0, nullptr, w_out, nullptr, y, tiles, ntiles, items, F, H, sb2, st);
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     return e;
 }

@@ -28,9 +28,13 @@ struct Tile {
 // counters (zeroed by the tile builder).  NULL buffers switch the split off.
 constexpr int kGemmPartSlots = 256;
 constexpr size_t kGemmPartSlotFloats = 256 * 256;    // the largest tile, BM x BN
+// Per-XCD work-item counters of the ping-pong GEMM's ordered fetch: 8 for the first
+// projection, 8 for the second, right after the part counters (and zeroed with them).
+constexpr int kGemmQueues = 16;
 struct SplitBuffers {
     float* parts;
     int* counts;
+    int* queue;       // this launch's 8 per-XCD counters (NULL: static order)
 };
 
 // Tile configurations of the bf16 grouped GEMM.  GEMM_M256 lets the tile builder choose
