@@ -58,7 +58,8 @@ def test_route_from_logits_bit_exact(lib, T, E, k, use_bias, flags):
 
 # T > 256 with bf16 x takes the split-weight bf16 MFMA gate (128-token tiles); ragged
 # K (H = 200), several expert tiles (E = 256) and a ragged expert count (E = 37)
-ROUTE_X_CASES = [(333, 200, 64, 2), (1000, 4096, 256, 8), (700, 64, 37, 3), (200, 512, 64, 2)]
+ROUTE_X_CASES = [(333, 200, 64, 2), (1000, 4096, 256, 8), (700, 64, 37, 3), (200, 512, 64, 2),
+                 (257, 8, 3, 1)]
 
 
 @pytest.mark.parametrize("T,H,E,k", ROUTE_X_CASES)
@@ -142,6 +143,8 @@ FFN_CASES = [  # T, H, E, k, F, ffn, dtype  (mean rows per expert picks the row 
     (1100, 520, 8, 2, 6400, "silu2", "bf16"), (1100, 520, 8, 2, 4608, "swiglu", "bf16"),
     (1024, 512, 16, 2, 4096, "silu2", "bf16"),
     (2048, 512, 8, 2, 4096, "silu2", "bf16"), (2048, 512, 8, 2, 4608, "swiglu", "bf16"),
+    # 256-row tiles with K >= 4096 in both projections: both take the ordered per-XCD fetch
+    (2048, 4096, 8, 2, 4096, "silu2", "bf16"),
 ]
 
 
