@@ -228,6 +228,26 @@ def test_forward_matches_oracle(lib, cfg):
         assert normwise(got[t], want) <= tol_for(cfg)
 
 
+@pytest.mark.parametrize("dtype,ffn", [("bf16", "silu2"), ("bf16", "swiglu"), ("f32", "swiglu")])
+def test_forward_all_tokens_to_two_experts(lib, dtype, ffn):
+    """Degenerate routing: a logit bias of 40 on experts 3 and 6 sends every token to both, so
+    six experts are empty (before, between and after the two) and each chosen one holds all
+    700 tokens in several row tiles (a ragged last one)."""
+    cfg = MoEConfig("collapsed", T=700, H=136, E=8, k=2, F=264, ffn=ffn, dtype=dtype, bias="none")
+    say(f"collapsed routing {cfg}")
+    d = generate(cfg)
+    d["bias"] = torch.zeros(cfg.E, dtype=torch.float32)
+    d["bias"][[3, 6]] = 40.0
+    inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    _, idx, _ = lib.route(inp["x"], inp["w_gate"], cfg.k, bias=inp["bias"])
+    assert set(np.unique(idx.cpu().numpy()).tolist()) == {3, 6}
+    out = run_forward(cfg, inp)
+    ref = _oracle_forward(cfg, d)
+    err = normwise(to_numpy(out), ref["out"])
+    say(f"  normwise error {err:.3e}")
+    assert err <= tol_for(cfg)
+
+
 def test_forward_is_deterministic(lib):
     cfg = MoEConfig("det", T=500, H=256, E=32, k=4, F=384, ffn="swiglu", dtype="bf16", bias="zipf1.1")
     say(f"determinism {cfg}")
