@@ -415,7 +415,11 @@ def test_page_flop_estimate_reproduced_by_accounting():
 # ------------------------------------------------------------- planted mistakes caught
 
 def _mut_silu_sigmoid(m):
-    m.setattr(O, "silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z, float))))
+    def sigmoid(z):
+        with np.errstate(over="ignore"):     # exp(-z) overflows to inf for very negative z
+            return 1.0 / (1.0 + np.exp(-np.asarray(z, float)))
+
+    m.setattr(O, "silu", sigmoid)
 
 
 def _mut_drop_up(m):
