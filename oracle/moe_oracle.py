@@ -20,7 +20,7 @@ Grouping tokens by expert (count, prefix sum, permutation, [Principles §5.1]) i
 exact reordering of step 4; the oracle performs it too so that the GPU's grouping
 tensors can be compared bit for bit.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   * selection is made on the logits (after the bias), not on rounded probabilities:
     softmax is strictly increasing, so the chosen set is the same in exact
     arithmetic; equal values go to the lower expert index; -0 equals +0.
