@@ -257,9 +257,16 @@ def test_forward_is_deterministic(lib):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cf", [0.5, 1.0])
-def test_forward_with_capacity(lib, cf):
-    cfg = MoEConfig("cap", T=300, H=128, E=8, k=2, F=192, ffn="swiglu", dtype="bf16", bias="normal0.5")
+CAP_CASES = [  # capacity factor, layer (mean rows per expert picks the row tile)
+    (0.5, MoEConfig("cap", T=300, H=128, E=8, k=2, F=192, ffn="swiglu", dtype="bf16", bias="normal0.5")),
+    (1.0, MoEConfig("cap", T=300, H=128, E=8, k=2, F=192, ffn="swiglu", dtype="bf16", bias="normal0.5")),
+    # 300 rows per expert on average: the 256- and 320-row tile kernels, capped experts full
+    (1.0, MoEConfig("cap_big", T=1200, H=264, E=8, k=2, F=392, ffn="silu2", dtype="bf16", bias="normal0.5")),
+]
+
+
+@pytest.mark.parametrize("cf,cfg", CAP_CASES, ids=[f"{c.name}-cf{f}" for f, c in CAP_CASES])
+def test_forward_with_capacity(lib, cf, cfg):
     say(f"capacity cf={cf} {cfg}")
     d = generate(cfg)
     inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
