@@ -131,6 +131,8 @@ def test_permute_bit_exact(lib, T, E, k, H, cap, dtype):
 FFN_CASES = [  # T, H, E, k, F, ffn, dtype  (mean rows per expert picks the row tile)
     (256, 128, 8, 2, 256, "swiglu", "f32"), (37, 72, 5, 2, 40, "silu2", "f32"),
     (24, 256, 16, 2, 512, "swiglu", "bf16"), (200, 200, 8, 2, 320, "silu2", "bf16"),
+    # decode-sized (16-row tiles) two-layer SiLU, F ragged against 256-column blocks
+    (40, 256, 16, 2, 384, "silu2", "bf16"),
     (512, 264, 4, 2, 136, "swiglu", "bf16"), (100, 128, 1, 1, 128, "silu2", "bf16"),
     (300, 128, 256, 8, 64, "swiglu", "bf16"), (700, 192, 4, 2, 2056, "swiglu", "bf16"),
     # ~275 rows per expert: the tile builder picks 320 x 192 tiles (8 items against ~16 x
