@@ -37,16 +37,18 @@ def _rand_layer(rng, T, H, E, F, ffn, bias=True):
 
 # ------------------------------------------------------------------ brute force (loops)
 
-def _brute_layer(x, wg, b, weights, k, ffn):
+def _brute_layer(x, wg, b, weights, k, ffn, forced=None, with_logits=False):
     """Pure-Python loops in the pages' order: logits, softmax over all experts,
     top-k on the probabilities, divide by the selected sum, run each selected
-    expert, weighted sum."""
+    expert, weighted sum.  ``forced[t]``, when given, replaces token t's top-k by
+    that list of experts (the gates are still renormalised over it)."""
     w_in, w_up, w_out = weights
     T, H = x.shape
     E = wg.shape[1]
     F = w_in.shape[2]
     out = np.zeros((T, H))
     sels = []
+    all_logits = []
     for t in range(T):
         logits = []
         for e in range(E):
@@ -59,6 +61,9 @@ def _brute_layer(x, wg, b, weights, k, ffn):
         tot = sum(z)
         p = [v / tot for v in z]
         sel = sorted(range(E), key=lambda e: (-p[e], e))[:k]
+        if forced is not None:
+            sel = list(forced[t])
+        all_logits.append(logits)
         ssum = sum(p[e] for e in sel)
         sels.append(sel)
         for j, e in enumerate(sel):
@@ -80,6 +85,8 @@ def _brute_layer(x, wg, b, weights, k, ffn):
                 for f in range(F):
                     s += hid[f] * w_out[e, f, i]
                 out[t, i] += g * s
+    if with_logits:
+        return out, np.array(sels, np.int32), np.array(all_logits)
     return out, np.array(sels, np.int32)
 
 
@@ -305,6 +312,7 @@ def pin_balance_uniform():
     idx = np.array([[t % E] for t in range(T)], np.int32)      # each expert T/E tokens
     logits = np.zeros((T, E))                                    # P_i = 1/E
     st = O.router_stats(logits, idx, E)
+    np.testing.assert_allclose(st["P"], 1.0 / E, rtol=1e-15)
     assert st["balance"] == pytest.approx(want, rel=1e-15)
     assert st["entropy"] == pytest.approx(math.log(E), rel=1e-15)
     # all tokens on one expert with confident probabilities -> far above 1
@@ -380,11 +388,82 @@ def pin_select_only_example():
     np.testing.assert_allclose(g32[0], [1 / (1 + e2), e2 / (1 + e2)], rtol=1e-14)
 
 
+def pin_token_output_bruteforce():
+    """One token's output for its own selection and for a forced one equals the
+    brute-force loops (probabilities over all experts, divided by the sum over the
+    selection), on every token of tiny layers."""
+    rng = np.random.default_rng(11)
+    for ffn in ("silu2", "swiglu"):
+        x, wg, b, w = _rand_layer(rng, 5, 4, 6, 5, ffn)
+        k = 3
+        want, sels, logits = _brute_layer(x, wg, b, w, k, ffn, with_logits=True)
+        # a forced selection: the experts ranked 2nd, 5th and 4th (not the top-k, and
+        # not in rank order)
+        order = np.argsort(-logits, axis=1, kind="stable")
+        forced = [[int(order[t, 1]), int(order[t, 4]), int(order[t, 3])] for t in range(x.shape[0])]
+        want_f, _ = _brute_layer(x, wg, b, w, k, ffn, forced=forced)
+        for t in range(x.shape[0]):
+            got = O.token_output(x[t], logits[t], sels[t], w, ffn)
+            np.testing.assert_allclose(got, want[t], rtol=1e-11, atol=1e-13)
+            got_f = O.token_output(x[t], logits[t], np.array(forced[t]), w, ffn)
+            np.testing.assert_allclose(got_f, want_f[t], rtol=1e-11, atol=1e-13)
+
+
+def pin_token_output_page_examples():
+    """Closed forms of one token's output with experts E_e(A) = c_e * SiLU(A)
+    (W1 = I, W2 = c_e * I):
+      * the walk-through probabilities [0.1, 0.6, 0.2, 0.1], selection [1, 2]:
+        gates 0.6 / 0.8 and 0.2 / 0.8, i.e. 0.75 * E1(A) + 0.25 * E2(A);
+      * the aggregation example 0.7 * E0(A) + 0.3 * E3(A), reached by forcing the
+        selection [0, 3] on probabilities [0.35, 0.25, 0.25, 0.15] (0.35 / 0.5 and
+        0.15 / 0.5), so that un-renormalised gates would give 0.35 and 0.15."""
+    ex = _gold("micro_examples.json")
+    H = E = 4
+    L3 = math.log(3.0)
+    A = np.array([L3, -L3, 0.0, 2 * L3])
+    silu_A = np.array([0.75 * L3, -0.25 * L3, 0.0, 2 * L3 * 0.9])
+    c = [1.0, -5.0, 7.0, 2.0]
+    w = (np.stack([np.eye(H)] * E), None, np.stack([c[e] * np.eye(H) for e in range(E)]))
+    tk = ex["topk_example"]
+    got = O.token_output(A, np.log(tk["probs"]), np.array(tk["indices"]), w, "silu2")
+    g1, g2 = tk["renormalised"]
+    e1, e2 = tk["indices"]
+    np.testing.assert_allclose(got, (g1 * c[e1] + g2 * c[e2]) * silu_A, rtol=1e-12, atol=1e-15)
+    wo = ex["weighted_output_example"]
+    e0, e3 = wo["experts"]
+    g0, g3 = wo["gates"]
+    got = O.token_output(A, np.log([0.35, 0.25, 0.25, 0.15]), np.array([e0, e3]), w, "silu2")
+    np.testing.assert_allclose(got, (g0 * c[e0] + g3 * c[e3]) * silu_A, rtol=1e-12, atol=1e-15)
+
+
+def pin_router_stats_hand_case():
+    """Statistics of four tokens over four experts whose softmax rows have closed
+    forms: logits [ln 3, 0, -inf, -inf] -> [3/4, 1/4, 0, 0]; [0, ln 3, -inf, -inf] ->
+    [1/4, 3/4, 0, 0]; [-inf, -inf, 0, 0] -> [0, 0, 1/2, 1/2]; [ln 4, -inf, -inf, 0] ->
+    [4/5, 0, 0, 1/5].  P_i is the mean probability of expert i (the balance loss's
+    P_i), top-1 confidence the mean of each row's largest probability.  Top-1 choices
+    (a tie to the lower index) are experts 0, 1, 2, 0: f = [1/2, 1/4, 1/4, 0]."""
+    ninf = -np.inf
+    L3, L4 = math.log(3.0), math.log(4.0)
+    logits = np.array([[L3, 0.0, ninf, ninf], [0.0, L3, ninf, ninf], [ninf, ninf, 0.0, 0.0],
+                       [L4, ninf, ninf, 0.0]])
+    idx = O.select_topk(logits, 1)
+    assert idx[:, 0].tolist() == [0, 1, 2, 0]
+    st = O.router_stats(logits, idx, 4)
+    P = [(0.75 + 0.25 + 0.8) / 4, (0.25 + 0.75) / 4, 0.5 / 4, (0.5 + 0.2) / 4]
+    np.testing.assert_allclose(st["P"], P, rtol=1e-14)
+    np.testing.assert_allclose(st["f"], [0.5, 0.25, 0.25, 0.0], rtol=0)
+    assert st["top1_mean"] == pytest.approx((0.75 + 0.75 + 0.5 + 0.8) / 4, rel=1e-14)
+    assert st["balance"] == pytest.approx(4 * (0.5 * P[0] + 0.25 * P[1] + 0.25 * P[2]), rel=1e-14)
+    assert st["entropy"] == pytest.approx(1.5 * math.log(2.0), rel=1e-14)
+
+
 PINS = [pin_no_renorm_example, pin_select_only_example, pin_page_shapes, pin_topk_example, pin_weighted_output_example, pin_ties,
         pin_topk_bruteforce, pin_grouping_bruteforce, pin_layer_bruteforce, pin_k_equals_E,
         pin_single_expert_is_dense_ffn, pin_dense_masked_equals_grouped, pin_silu_closed_form,
         pin_selection_matrix_ffn, pin_f32_bias_add_is_one_rounding, pin_gate_invariants,
-        pin_balance_uniform, pin_capacity_bruteforce, pin_alternatives]
+        pin_balance_uniform, pin_capacity_bruteforce, pin_alternatives,
+        pin_token_output_bruteforce, pin_token_output_page_examples, pin_router_stats_hand_case]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -513,10 +592,45 @@ def _mut_renorm_ignored(m):
     m.setattr(O, "renormalised_gates", lambda l, idx, renorm=True: orig(l, idx, True))
 
 
+def _mut_token_output_no_renorm(m):
+    def tok(x_row, logits_row, sel, weights, ffn):
+        x_row = np.asarray(x_row, float)[None, :]
+        p = O.softmax(np.asarray(logits_row, float)[None, :])[0]
+        out = np.zeros(x_row.shape[1])
+        for e in sel:
+            w_in, w_up, w_out = O._expert_weights(weights, int(e))
+            out += p[e] * O.expert_ffn(x_row, w_in, w_up, w_out, ffn)[0]
+        return out
+    m.setattr(O, "token_output", tok)
+
+
+def _mut_stats_P_is_top1_share(m):
+    orig = O.router_stats
+
+    def st(logits, idx, E):
+        r = orig(logits, idx, E)
+        top1 = np.asarray(idx)[:, 0]
+        r["P"] = np.bincount(top1, minlength=E) / top1.size
+        r["balance"] = float(E * np.sum(r["f"] * r["P"]))
+        return r
+    m.setattr(O, "router_stats", st)
+
+
+def _mut_stats_top1_constant(m):
+    orig = O.router_stats
+
+    def st(logits, idx, E):
+        r = orig(logits, idx, E)
+        r["top1_mean"] = 1.0 / E
+        return r
+    m.setattr(O, "router_stats", st)
+
+
 MUTANTS = [_mut_silu_sigmoid, _mut_drop_up, _mut_no_renorm, _mut_smallest, _mut_tie_high,
            _mut_combine_wrong_index, _mut_unstable_group, _mut_transposed_down, _mut_no_bias,
            _mut_capacity_off_by_one, _mut_gates_sign, _mut_select_only_ignored,
-           _mut_renorm_ignored]
+           _mut_renorm_ignored, _mut_token_output_no_renorm, _mut_stats_P_is_top1_share,
+           _mut_stats_top1_constant]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m.__name__ for m in MUTANTS])
