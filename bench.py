@@ -1,18 +1,22 @@
 """Benchmark of the MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--others NAME,NAME,... | --others none]
 
 A step is one whole layer forward (gate projection, top-k, grouping, grouped expert
-FFN, combine) over one batch of synthetic inputs resident in HBM.  The default
-workload is the pages' worked shape: 8192 tokens (batch 4 x seq 2048), hidden 4096,
-64 experts, top-2, two-layer SiLU FFN 4096 -> 16384 -> 4096, bf16 with fp32 routing.
+FFN, combine) over one batch of synthetic inputs resident in HBM.  The headline
+workload is the largest configuration that fits one GPU: the fine-grained, skewed
+layer (8192 tokens, hidden 7168, 256 SwiGLU experts of d_ff 2048, top-8, a Zipf-by-
+rank logit bias), bf16 with fp32 routing.
 
 Prints one JSON line: tokens/s, the roofline figures of the dominant grouped-GEMM kernel
-(timed live with HIP events that moe_forward records at its stage boundaries on its
-stream; the other projection is reported beside it), per-stage times and rates, the
+(timed live with HIP events that moe_forward_timed records at its stage boundaries on
+its stream; the other projection is reported beside it), per-stage times and rates, the
 layer time's median and p10/p90 with and without a 256 MB MALL flush before each step,
 peak rates measured on this GPU (bf16 MFMA loop, HBM read and copy) beside the published
-ones, and the CPU oracle timed on a bounded sample of the same workload.
+ones, the CPU oracle timed on a bounded sample of the same workload, and under
+"workloads" the same per-workload figures (tokens/s, grouped-GEMM TFLOP/s and % of bf16
+peak, per-projection rooflines, stages) for the other layer shapes.
 """
 from __future__ import annotations
 
@@ -26,23 +30,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
+HEADLINE = "fine_grained_skewed"
+OTHERS = ["pages_worked_shape", "mixtral_style", "decode"]
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="pages_worked_shape")
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--others", default=",".join(OTHERS),
+                    help="comma-separated workloads measured beside the headline ('none': no others)")
+    ap.add_argument("--other-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--flush-steps", type=int, default=5,
                     help="extra steps, each after a 1 GiB write that evicts the MALL (0: none)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the peak-rate microbenchmarks")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def main():
@@ -54,24 +63,14 @@ def main():
               "tokens.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    import mixture_experts_layer_46_amd as M
     from mixture_experts_layer_46_amd import _lib
-    from mixture_experts_layer_46_amd import accounting as A
-    from workloads import generate, preset
+    from workloads import preset
 
-    cfg = preset(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     _lib.load()
-    inp = generate(cfg, device=dev)
-    x, wg, b = inp["x"], inp["w_gate"], inp["bias"]
-    w_in, w_up, w_out = inp["w_in"], inp["w_up"], inp["w_out"]
-    out = torch.empty_like(x)
-    ws = M.Workspace(dev)
-    torch.cuda.synchronize()
 
     if args.copy_calibration:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
@@ -81,20 +80,74 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # routing statistics of this batch (outside the timed region)
-    logits, idx, _ = M.route(x, wg, cfg.k, bias=b)
-    grp = M.permute(idx, cfg.E)
-    counts = grp["counts"].cpu().numpy()
-    touched = int((counts > 0).sum())
+    cfg = preset(args.config)
+    head = measure(cfg, dev, args.steps, args.warmup, args.flush_steps,
+                   cpu_tokens=None if args.no_cpu_baseline else args.cpu_tokens)
+    others = [] if args.others in ("", "none") else [o for o in args.others.split(",") if o != cfg.name]
+    extra = {}
+    for name in others:
+        r = measure(preset(name), dev, args.other_steps, max(2, args.warmup // 2), 0, None)
+        extra[name] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "layer_ms", "config", "dtype",
+                                         "grouped_gemm_tflops", "grouped_gemm_pct_bf16_peak",
+                                         "grouped_ffn_ms", "grouped_ffn_pct_roofline", "touched_experts",
+                                         "projections", "stages")}
+        extra[name]["steps"] = args.other_steps
 
-    def step():
-        M.forward(x, wg, w_in, w_up, w_out, cfg.k, bias=b, out=out, workspace=ws)
+    result = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": head["config"],
+        "grouped_gemm_tflops": head["grouped_gemm_tflops"],
+        "grouped_gemm_pct_bf16_peak": head["grouped_gemm_pct_bf16_peak"],
+        "grouped_ffn_ms": head["grouped_ffn_ms"],
+        "grouped_ffn_pct_roofline": head["grouped_ffn_pct_roofline"],
+        "touched_experts": head["touched_experts"],
+        "roofline": head["roofline"],
+        "projections": head["projections"],
+        "layer_ms": head["layer_ms"],
+        "layer_ms_mall_flushed": head["layer_ms_mall_flushed"],
+        "stages": head["stages"],
+        "workloads": extra,
+        "measured_peaks": None if args.no_peaks else measured_peaks(dev),
+        "cpu_baseline": head["cpu_baseline"],
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
-    for _ in range(args.warmup):
-        step()
+
+def measure(cfg, dev, steps, warmup, flush_steps, cpu_tokens):
+    """Time `steps` layer forwards of workload `cfg` (after `warmup` untimed ones) with
+    stage events; returns the figures of one workload (and, with cpu_tokens, the CPU
+    oracle on that many of its tokens)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_46_amd as M
+    from mixture_experts_layer_46_amd import _lib
+    from mixture_experts_layer_46_amd import accounting as A
+    from workloads import generate
+
+    inp = generate(cfg, device=dev)
+    x, wg, b = inp["x"], inp["w_gate"], inp["bias"]
+    w_in, w_up, w_out = inp["w_in"], inp["w_up"], inp["w_out"]
+    out = torch.empty_like(x)
+    ws = M.Workspace(dev)
     torch.cuda.synchronize()
 
-    K = args.steps
+    def step(events=None):
+        M.forward(x, wg, w_in, w_up, w_out, cfg.k, bias=b, out=out, workspace=ws, events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # the routing this batch takes (the forward's own, from its workspace; not timed)
+    mid = M.forward_intermediates(ws, x, wg, w_in, w_up, cfg.k)
+    counts = mid["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+
+    K = steps
     NS = _lib.MOE_STAGE_EVENTS
 
     def new_events(n):
@@ -109,11 +162,9 @@ def main():
 
     t0 = time.perf_counter()
     for i in range(K):
-        _lib.set_stage_events(ev[i])
-        step()
+        step(ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.set_stage_events(None)
 
     ms_step = (t1 - t0) * 1e3 / K
     # stage durations per step: [route, group, ffn up, ffn down, combine]
@@ -127,16 +178,14 @@ def main():
     # the same steps after a 1 GiB write each, so x and the routing tensors start out of the
     # 256 MB MALL (not part of the timed loop above)
     flushed = None
-    if args.flush_steps > 0:
+    if flush_steps > 0:
         junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        evf = new_events(args.flush_steps)
+        evf = new_events(flush_steps)
         torch.cuda.synchronize()
-        for i in range(args.flush_steps):
+        for i in range(flush_steps):
             junk.fill_(i & 0xFF)
-            _lib.set_stage_events(evf[i])
-            step()
+            step(evf[i])
         torch.cuda.synchronize()
-        _lib.set_stage_events(None)
         flushed = _spread([row[0].elapsed_time(row[-1]) for row in evf])
         del junk
 
@@ -145,22 +194,27 @@ def main():
     peak_flops = A.PEAK_BF16_FLOPS if cfg.dtype == "bf16" else A.PEAK_FP32_FLOPS
     kernels = {
         "up": dict(name=_gemm_kernel_name(cfg, True, counts), ms=up_ms,
-                   flops=A.ffn_up_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn), bytes=sb.ffn_up),
+                   flops=A.ffn_up_flops(cfg.T, cfg.k, cfg.H, cfg.F, cfg.ffn), bytes=sb.ffn_up,
+                   designed_bytes=sb.ffn_up_designed),
         "down": dict(name=_gemm_kernel_name(cfg, False, counts), ms=down_ms,
-                     flops=A.ffn_down_flops(cfg.T, cfg.k, cfg.H, cfg.F), bytes=sb.ffn_down),
+                     flops=A.ffn_down_flops(cfg.T, cfg.k, cfg.H, cfg.F), bytes=sb.ffn_down,
+                     designed_bytes=sb.ffn_down_designed),
     }
-    for kd in kernels.values():
-        kd["roofline"] = _roofline(kd, peak_flops)
+    projections = {}
+    for which, kd in kernels.items():
+        r = _roofline(kd, peak_flops)
+        r.update(kernel=kd["name"], ms=kd["ms"], algorithmic_bytes=kd["bytes"], algorithmic_flops=kd["flops"],
+                 as_designed_bytes=kd["designed_bytes"],
+                 as_designed_GBps=kd["designed_bytes"] / (kd["ms"] * 1e-3) / 1e9,
+                 tflops=kd["flops"] / (kd["ms"] * 1e-3) / 1e12,
+                 pct_bf16_peak=kd["flops"] / (kd["ms"] * 1e-3) / A.PEAK_BF16_FLOPS * 100,
+                 traffic=_traffic(cfg.name, which, kd["name"]))
+        projections[which] = r
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    roof = dict(kernels[dom]["roofline"])
-    roof["traffic"] = _traffic(cfg.name, dom, kernels[dom]["name"])
-    roof["kernel"] = kernels[dom]["name"]
-    roof["ms"] = kernels[dom]["ms"]
-    roof["algorithmic_bytes"] = kernels[dom]["bytes"]
-    roof["algorithmic_flops"] = kernels[dom]["flops"]
-    other = "down" if dom == "up" else "up"
-    roof["other_projection"] = dict(kernels[other]["roofline"], kernel=kernels[other]["name"],
-                                    ms=kernels[other]["ms"])
+    roof = {k: projections[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof.update(kernel=kernels[dom]["name"], projection=dom, ms=kernels[dom]["ms"],
+                algorithmic_bytes=kernels[dom]["bytes"], algorithmic_flops=kernels[dom]["flops"],
+                roofline_ms=projections[dom]["roofline_ms"])
     t_ffn_roof = max(flops / peak_flops, (sb.ffn_up + sb.ffn_down) / A.PEAK_HBM_BPS)
     sec = ffn_ms * 1e-3
 
@@ -172,17 +226,12 @@ def main():
         "route": dict(hbm_stage(float(per[:, 0].mean()), sb.route),
                       gate_tflops=A.gate_flops(cfg.T, cfg.H, cfg.E) / (per[:, 0].mean() * 1e-3) / 1e12),
         "group": hbm_stage(float(per[:, 1].mean()), sb.group),
-        "ffn_up": dict(hbm_stage(up_ms, sb.ffn_up), tflops=kernels["up"]["flops"] / (up_ms * 1e-3) / 1e12),
-        "ffn_down": dict(hbm_stage(down_ms, sb.ffn_down),
-                         tflops=kernels["down"]["flops"] / (down_ms * 1e-3) / 1e12),
+        "ffn_up": dict(hbm_stage(up_ms, sb.ffn_up), tflops=projections["up"]["tflops"]),
+        "ffn_down": dict(hbm_stage(down_ms, sb.ffn_down), tflops=projections["down"]["tflops"]),
         "combine": hbm_stage(float(per[:, 4].mean()), sb.combine),
     }
-
-    result = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
-        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+    res = {
+        "tokens_per_s": tokens_per_s, "ms_per_step": ms_step, "dtype": cfg.dtype,
         "config": {"workload": cfg.name, "tokens": cfg.T, "batch": cfg.batch, "seq_len": cfg.seq,
                    "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.F,
                    "ffn": cfg.ffn, "bias": cfg.bias, "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
@@ -192,16 +241,17 @@ def main():
         "grouped_ffn_pct_roofline": t_ffn_roof / sec * 100,
         "touched_experts": touched,
         "roofline": roof,
+        "projections": projections,
         "layer_ms": _spread(layer.tolist()),
         "layer_ms_mall_flushed": flushed,
         "stages": stages,
-        "measured_peaks": None if args.no_peaks else measured_peaks(dev),
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
-    print(json.dumps(result), flush=True)
-    return 0
+    if cpu_tokens:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, cpu_tokens)
+    del inp, x, wg, b, w_in, w_up, w_out, out, ws, mid
+    torch.cuda.empty_cache()
+    return res
 
 
 def _spread(ms):

@@ -39,9 +39,10 @@
  *   - No C++ exception crosses this interface.
  *
  * Limits of this version: 1 <= E <= 256; 1 <= k <= min(E, 8); H % 8 == 0; F % 8 == 0;
- * T * k < 2^31; T*H and T*k*max(H,F) < 2^62 elements; x (T*H elements) and one expert
- * matrix with 128 extra rows ((H+128)*F and (F+128)*H elements) below 4 GiB each, since
- * the grouped GEMM addresses them with 32-bit byte offsets (MOE_ERR_UNSUPPORTED otherwise).
+ * T * k < 2^31; T*k*max(H,F) < 4e18 elements; x (T*H elements) and one expert matrix
+ * with 128 extra rows ((H+128)*F and (F+128)*H elements) below 2 GiB each, since the
+ * grouped GEMM reads them through buffer resources with 32-bit byte offsets and an
+ * out-of-range marker at 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -91,12 +92,40 @@ typedef struct {
                             With C > 0 the pairs of expert e beyond its first C (in token
                             order) are dropped: they get no grouped row and add nothing
                             to the output ([Principles §4.3] capacity factor:
-                            C = ceil(capacity_factor * T * k / E), computed by the caller). */
+                            C = ceil(capacity_factor * T * k / E), see moe_capacity_rows). */
 } moe_shape;
+
+/* Per-expert row limit of a capacity factor, for moe_shape.capacity.  [Principles §4.3]
+ * The page's capacity = capacity_factor * (total_tokens / num_experts), with the total
+ * read as token-expert pairs T*k:  *rows = max(1, ceil(capacity_factor * (T*k) / E)),
+ * evaluated in double precision.  capacity_factor must be positive and finite, T >= 0,
+ * k, E > 0 (MOE_ERR_SHAPE otherwise; MOE_ERR_NULL if rows is NULL).  Host only. */
+moe_status moe_capacity_rows(double capacity_factor, int64_t T, int32_t k, int32_t E, int32_t* rows);
 
 /* Bytes of device workspace that moe_forward needs for `shape`; the same size is
  * enough for moe_permute and moe_grouped_ffn.  Host only; enqueues nothing. */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Where moe_forward keeps its intermediates inside the workspace: byte offsets from the
+ * workspace base, for inspecting a finished call (tests, debugging).  After
+ * moe_forward on `shape` has completed, the workspace holds
+ *   logit_parts  [logit_splits][T][E] fp32: partial sums of x @ W_g over logit_splits
+ *                consecutive ranges of H (no bias); top-k adds them in range order,
+ *                then adds the bias once
+ *   topk_idx     [T, k] int32, topk_w [T, k] fp32: the routing the layer used
+ *   counts       [E] int32, offsets [E+1] int32, sorted_token [T*k] int32,
+ *   row_of_pair  [T*k] int32: the grouping, as moe_permute defines them
+ *   h            [offsets[E], F] dtype: first-projection output, grouped rows
+ *   y            [offsets[E], H] dtype: second-projection output (y_perm)
+ * total is moe_workspace_size().  The contents are undefined before the call ends or
+ * after another call reuses the workspace.  Host only; enqueues nothing. */
+typedef struct {
+    size_t  logit_parts;
+    int32_t logit_splits;
+    int32_t reserved;
+    size_t  topk_idx, topk_w, counts, offsets, sorted_token, row_of_pair, h, y, total;
+} moe_workspace_parts;
+moe_status moe_workspace_layout(const moe_shape* shape, moe_workspace_parts* parts);
 
 /* Gate projection, top-k and gates.  [FourStage §2.1-§2.2], [Principles §2.1-§2.2, §2.4]
  *   x        [T, H] dtype, or NULL: then `logits` is an INPUT of fp32 logits (no bias)
@@ -173,9 +202,9 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
                             const int32_t* counts, const int32_t* offsets, float* stats,
                             hipStream_t stream);
 
-/* Timing hook for benchmarks.  With `events` pointing to MOE_STAGE_EVENTS events (the
- * caller's, created with timing enabled) and n == MOE_STAGE_EVENTS, later moe_forward
- * calls made by the calling thread record them on their stream at the stage boundaries:
+/* moe_forward with timing events, for benchmarks.  `events` is NULL (then this is
+ * moe_forward) or MOE_STAGE_EVENTS events of the caller, created with timing enabled,
+ * which are recorded on `stream` at the stage boundaries:
  *   [0] before the gate projection
  *   [1] after top-k and gates (the routing stage, [FourStage §2.1-§2.2])
  *   [2] after the grouping (histogram, offsets, maps, the GEMM tile list, [Principles §5.1]),
@@ -184,11 +213,13 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
  *   [4] after the second projection
  *   [5] after the combine ([FourStage §2.4])
  * so hipEventElapsedTime between neighbours gives each stage's duration, and [2]-[3],
- * [3]-[4] each projection kernel's.  events == NULL with n == 0 switches the hook off.
- * A NULL array with n != 0 or a NULL entry is MOE_ERR_NULL; any other n is
- * MOE_ERR_SHAPE.  The array is copied; host only. */
+ * [3]-[4] each projection kernel's.  A NULL entry is MOE_ERR_NULL.  Nothing is kept
+ * after the call returns. */
 #define MOE_STAGE_EVENTS 6
-moe_status moe_set_stage_events(const hipEvent_t* events, int n);
+moe_status moe_forward_timed(const moe_shape* shape, const void* x, const float* w_gate,
+                             const float* bias, const void* w_in, const void* w_up,
+                             const void* w_out, void* out, void* workspace, size_t ws_bytes,
+                             const hipEvent_t* events, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);

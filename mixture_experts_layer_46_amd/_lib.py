@@ -7,7 +7,6 @@ There is no fallback: if the library is missing or a call fails, an exception sa
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -22,9 +21,10 @@ MOE_FLAG_NO_RENORM = 0x2
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
 
-EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_router_stats", "moe_set_stage_events", "moe_status_str",
-           "moe_last_error", "moe_peak_mfma_bf16", "moe_peak_hbm_read", "moe_peak_hbm_copy"]
+EXPORTS = ["moe_workspace_size", "moe_workspace_layout", "moe_capacity_rows", "moe_route",
+           "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
+           "moe_router_stats", "moe_status_str", "moe_last_error", "moe_peak_mfma_bf16",
+           "moe_peak_hbm_read", "moe_peak_hbm_copy"]
 
 MOE_STAGE_EVENTS = 6
 
@@ -33,6 +33,14 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("ffn", ctypes.c_int32), ("flags", ctypes.c_uint32), ("capacity", ctypes.c_int32)]
+
+
+class MoeWorkspaceParts(ctypes.Structure):
+    _fields_ = [("logit_parts", ctypes.c_size_t), ("logit_splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("topk_idx", ctypes.c_size_t),
+                ("topk_w", ctypes.c_size_t), ("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t),
+                ("sorted_token", ctypes.c_size_t), ("row_of_pair", ctypes.c_size_t),
+                ("h", ctypes.c_size_t), ("y", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class MoeError(RuntimeError):
@@ -59,19 +67,21 @@ def load(path: str = LIB_PATH):
     st = ctypes.c_void_p
     sig = {
         "moe_workspace_size": [sp, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_workspace_layout": [sp, ctypes.POINTER(MoeWorkspaceParts)],
+        "moe_capacity_rows": [ctypes.c_double, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                              ctypes.POINTER(ctypes.c_int32)],
         "moe_route": [sp, vp, f32p, f32p, f32p, i32p, f32p, st],
         "moe_permute": [sp, i32p, vp, i32p, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, st],
         "moe_grouped_ffn": [sp, vp, i32p, vp, vp, vp, vp, vp, ctypes.c_size_t, st],
         "moe_combine": [sp, vp, i32p, f32p, vp, st],
         "moe_forward": [sp, vp, f32p, f32p, vp, vp, vp, vp, vp, ctypes.c_size_t, st],
+        "moe_forward_timed": [sp, vp, f32p, f32p, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, st],
         "moe_router_stats": [sp, f32p, f32p, i32p, i32p, f32p, st],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.moe_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
-    lib.moe_set_stage_events.restype = ctypes.c_int
     lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.POINTER(ctypes.c_int), st]
     lib.moe_peak_mfma_bf16.restype = ctypes.c_int
     lib.moe_peak_hbm_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, st]
@@ -92,10 +102,13 @@ def _check(fn: str, code: int):
 
 
 def capacity_rows(capacity_factor: float | None, T: int, k: int, E: int) -> int:
-    """Per-expert row limit C = ceil(cf * T * k / E) (0 = no limit)."""
+    """moe_shape.capacity for a capacity factor (the library's moe_capacity_rows), or 0
+    (no limit) for None."""
     if capacity_factor is None:
         return 0
-    return max(1, int(math.ceil(capacity_factor * (T * k) / E)))
+    rows = ctypes.c_int32(0)
+    _check("moe_capacity_rows", load().moe_capacity_rows(float(capacity_factor), T, k, E, ctypes.byref(rows)))
+    return rows.value
 
 
 @dataclass
@@ -134,6 +147,14 @@ def workspace_size(shape: Shape) -> int:
     return n.value
 
 
+def workspace_layout(shape: Shape) -> dict:
+    """Byte offsets of moe_forward's intermediates in its workspace (moe_workspace_layout)."""
+    p = MoeWorkspaceParts()
+    s = shape.c()
+    _check("moe_workspace_layout", load().moe_workspace_layout(ctypes.byref(s), ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in MoeWorkspaceParts._fields_ if name != "reserved"}
+
+
 def route(shape: Shape, x, w_gate, bias, logits, topk_idx, topk_w, stream=None):
     s = shape.c()
     _check("moe_route", load().moe_route(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
@@ -166,13 +187,23 @@ def combine(shape: Shape, y_perm, row_of_pair, topk_w, out, stream=None):
                                              _ptr(topk_w), _ptr(out), _stream(stream)))
 
 
-def forward(shape: Shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, stream=None):
+def forward(shape: Shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, stream=None,
+            events=None):
+    """moe_forward, or moe_forward_timed when `events` (MOE_STAGE_EVENTS torch.cuda.Event
+    objects with timing, recorded at the stage boundaries) is given."""
     s = shape.c()
-    _check("moe_forward", load().moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
-                                             _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
-                                             _ptr(workspace),
-                                             workspace.numel() * workspace.element_size(),
-                                             _stream(stream)))
+    nbytes = workspace.numel() * workspace.element_size()
+    if events is None:
+        _check("moe_forward", load().moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
+                                                 _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
+                                                 _ptr(workspace), nbytes, _stream(stream)))
+        return
+    if len(events) != MOE_STAGE_EVENTS:
+        raise ValueError(f"expected {MOE_STAGE_EVENTS} events, got {len(events)}")
+    arr = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*[e.cuda_event for e in events])
+    _check("moe_forward_timed", load().moe_forward_timed(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
+                                                         _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
+                                                         _ptr(workspace), nbytes, arr, _stream(stream)))
 
 
 def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None):
@@ -180,18 +211,6 @@ def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None
     _check("moe_router_stats", load().moe_router_stats(ctypes.byref(s), _ptr(logits), _ptr(bias),
                                                        _ptr(counts), _ptr(offsets), _ptr(stats),
                                                        _stream(stream)))
-
-
-def set_stage_events(events=None):
-    """Record MOE_STAGE_EVENTS torch.cuda.Event objects at the stage boundaries of later
-    forward calls on this thread: before routing, after routing, after grouping (= before
-    the first expert projection), between the projections, after the second projection,
-    after the combine.  None switches it off."""
-    if events is None:
-        _check("moe_set_stage_events", load().moe_set_stage_events(None, 0))
-        return
-    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
-    _check("moe_set_stage_events", load().moe_set_stage_events(arr, len(events)))
 
 
 def peak_mfma_bf16(blocks: int, iters: int, sink, clocks, stream=None) -> int:

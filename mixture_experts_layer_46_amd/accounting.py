@@ -59,12 +59,21 @@ def expert_weight_bytes(H: int, F: int, ffn: str, dtype: str) -> int:
 
 @dataclass
 class StageBytes:
-    """Algorithmic HBM bytes of each stage, given the number of experts touched."""
+    """HBM bytes of each stage, given the number of experts touched.
+
+    Algorithmic bytes are the least the layer must move: every touched expert's
+    weights once, x read once, out written once.  Split over the two projections, the
+    first takes its weights and x, the second its weights and out (the grouped rows in
+    between, h and the y rows, are the design's, not the method's).  The as-designed
+    figures add them: h written by the first projection and read by the second, the y
+    rows written by the second (and read by the combine)."""
     route: int
     permute: int       # the explicit grouping with the row gather (moe_permute with x)
     group: int         # moe_forward's grouping: top-k indices in, the two maps out
-    ffn_up: int        # first grouped GEMM: touched W_in (+W_up) + x once + h out
-    ffn_down: int      # second grouped GEMM: touched W_out + h in + y rows out
+    ffn_up: int        # first projection, algorithmic: touched W_in (+W_up) + x
+    ffn_down: int      # second projection, algorithmic: touched W_out + out
+    ffn_up_designed: int     # + h written
+    ffn_down_designed: int   # + h read + y rows written
     combine: int
     layer: int         # the whole layer: touched weights once + x in + out
 
@@ -77,9 +86,11 @@ def stage_bytes(T: int, H: int, E: int, k: int, F: int, ffn: str, dtype: str,
     permute = T * H * b + P * H * b + P * 16
     w_up_side = (n_mats(ffn) - 1) * H * F * b * touched
     w_down_side = F * H * b * touched
-    ffn_up = w_up_side + T * H * b + P * F * b      # rows are gathered from x itself
-    ffn_down = w_down_side + P * F * b + P * H * b
+    ffn_up = w_up_side + T * H * b
+    ffn_down = w_down_side + T * H * b
     group = P * 4 + P * 8
     combine = P * H * b + T * H * b + P * 8
     layer = w_up_side + w_down_side + 2 * T * H * b
-    return StageBytes(route, permute, group, ffn_up, ffn_down, combine, layer)
+    return StageBytes(route, permute, group, ffn_up, ffn_down,
+                      w_up_side + T * H * b + P * F * b,
+                      w_down_side + P * F * b + P * H * b, combine, layer)

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer forward: argument checks, workspace carve-up, launches.
 // Declarations, argument meaning, layouts, ownership and error behaviour: include/moe.h.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -16,9 +17,6 @@ namespace moe {
 namespace {
 
 thread_local std::string g_last_error;
-// timing hook of moe_set_stage_events: the stage boundaries of moe_forward, or off
-thread_local hipEvent_t g_stage_ev[MOE_STAGE_EVENTS] = {};
-thread_local bool g_stage_on = false;
 
 moe_status fail(moe_status st, const char* fmt, ...) {
     char buf[512];
@@ -106,13 +104,16 @@ moe_status check_shape(const moe_shape* s) {
     if (s->T >= (1ll << 31) || P >= (1ll << 31)) return fail(MOE_ERR_SHAPE, "T*k = %lld >= 2^31", P);
     const long long mx = s->H > s->F ? s->H : s->F;
     if ((double)P * (double)mx >= 4.0e18) return fail(MOE_ERR_SHAPE, "T*k*max(H,F) too large");
-    // the grouped GEMM addresses one expert matrix (plus up to 128 rows past its end) and
-    // the token matrix x with 32-bit byte offsets
+    // the grouped GEMM reads one expert matrix (plus up to 128 rows past its end) and the
+    // token matrix x through buffer resources with 32-bit byte offsets, and marks a chunk
+    // it must not load with the offset 2^31, which reads zeros only while the buffer is
+    // shorter than that
     const long long es = s->dtype == MOE_F32 ? 4 : 2;
-    if (((long long)s->H + 128) * s->F * es >= (1ll << 32) || ((long long)s->F + 128) * s->H * es >= (1ll << 32))
-        return fail(MOE_ERR_UNSUPPORTED, "one expert matrix (H=%d x F=%d) must stay below 4 GiB", s->H, s->F);
-    if (s->T * (long long)s->H * es >= (1ll << 32))
-        return fail(MOE_ERR_UNSUPPORTED, "x (T=%lld x H=%d) must stay below 4 GiB", (long long)s->T, s->H);
+    if (((long long)s->H + 128) * s->F * es >= (1ll << 31) || ((long long)s->F + 128) * s->H * es >= (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "one expert matrix (H=%d x F=%d, plus 128 rows) must stay below 2 GiB",
+                    s->H, s->F);
+    if (s->T * (long long)s->H * es >= (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "x (T=%lld x H=%d) must stay below 2 GiB", (long long)s->T, s->H);
     return MOE_OK;
 }
 
@@ -285,9 +286,9 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
     return MOE_OK;
 }
 
-moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
-                       const void* w_in, const void* w_up, const void* w_out, void* out,
-                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+moe_status moe_forward_timed(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                             const void* w_in, const void* w_up, const void* w_out, void* out,
+                             void* workspace, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape& s = *shape;
@@ -300,6 +301,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     if (s.ffn == MOE_FFN_SWIGLU) REQ(w_up, "w_up");
     else if (w_up) return fail(MOE_ERR_SHAPE, "w_up must be NULL for the SiLU two-layer FFN");
     if ((st = check_ws(s, workspace, ws_bytes)) != MOE_OK) return st;
+    if (events)
+        for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
+            if (events[i] == nullptr) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
     if (s.T == 0) return MOE_OK;
     (void)hipGetLastError();
     const Layout L = layout_of(s);
@@ -311,10 +315,10 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     int32_t* sorted_token = at<int32_t>(workspace, L.sorted_token);
     int32_t* row_of_pair = at<int32_t>(workspace, L.row_of_pair);
     const int splits = gate_splits(s.T, s.H, s.E, s.dtype);
-    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[0], stream), "stage event");
+    if (events) HIPCHK(hipEventRecord(events[0], stream), "stage event");
     HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, stream), "gate_logits");
     HIPCHK(launch_topk(logits, splits, nullptr, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");
-    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[1], stream), "stage event");
+    if (events) HIPCHK(hipEventRecord(events[1], stream), "stage event");
     HIPCHK(launch_group(idx, P, s.k, s.E, s.capacity, at<int32_t>(workspace, L.segcnt),
                         at<int32_t>(workspace, L.counts), offsets, sorted_token, row_of_pair, stream),
            "group");
@@ -322,11 +326,50 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
     // events 2..4 are recorded by the grouped FFN (before, between and after its two
     // projections; the tile list is built before event 2).
     st = run_grouped(s, x, sorted_token, offsets, w_in, w_up, w_out, at<void>(workspace, L.y),
-                     workspace, g_stage_on ? g_stage_ev + 2 : nullptr, stream);
+                     workspace, events ? events + 2 : nullptr, stream);
     if (st != MOE_OK) return st;
     HIPCHK(launch_combine(at<void>(workspace, L.y), row_of_pair, gw, out, s.T, s.k, s.H, s.dtype, stream),
            "combine");
-    if (g_stage_on) HIPCHK(hipEventRecord(g_stage_ev[5], stream), "stage event");
+    if (events) HIPCHK(hipEventRecord(events[5], stream), "stage event");
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                       const void* w_in, const void* w_up, const void* w_out, void* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return moe_forward_timed(shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_workspace_layout(const moe_shape* shape, moe_workspace_parts* parts) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!parts) return fail(MOE_ERR_NULL, "parts is NULL");
+    const Layout L = layout_of(*shape);
+    moe_workspace_parts p{};
+    p.logit_parts = L.logits;
+    p.logit_splits = gate_splits(shape->T, shape->H, shape->E, shape->dtype);
+    p.topk_idx = L.topk_idx;
+    p.topk_w = L.topk_w;
+    p.counts = L.counts;
+    p.offsets = L.offsets;
+    p.sorted_token = L.sorted_token;
+    p.row_of_pair = L.row_of_pair;
+    p.h = L.h;
+    p.y = L.y;
+    p.total = L.total;
+    *parts = p;
+    return MOE_OK;
+}
+
+moe_status moe_capacity_rows(double capacity_factor, int64_t T, int32_t k, int32_t E, int32_t* rows) {
+    if (!rows) return fail(MOE_ERR_NULL, "rows is NULL");
+    if (!(capacity_factor > 0.0) || !(capacity_factor < 1e9))
+        return fail(MOE_ERR_SHAPE, "capacity_factor = %g must be positive and finite", capacity_factor);
+    if (T < 0 || k <= 0 || E <= 0) return fail(MOE_ERR_SHAPE, "T = %lld, k = %d, E = %d", (long long)T, k, E);
+    // C = ceil(capacity_factor * (T * k) / E), in double; at least 1 (0 means no limit)
+    const double c = std::ceil(capacity_factor * (double)(T * (long long)k) / (double)E);
+    if (c >= 2147483647.0) return fail(MOE_ERR_SHAPE, "capacity %g does not fit int32", c);
+    *rows = c < 1.0 ? 1 : (int32_t)c;
     return MOE_OK;
 }
 
@@ -346,20 +389,6 @@ moe_status moe_router_stats(const moe_shape* shape, const float* logits, const f
     (void)hipGetLastError();
     HIPCHK(launch_router_stats(logits, bias, counts, offsets, stats, s.T, s.E, s.k, s.capacity, stream),
            "router_stats");
-    return MOE_OK;
-}
-
-moe_status moe_set_stage_events(const hipEvent_t* events, int n) {
-    if (events == nullptr && n == 0) {
-        g_stage_on = false;
-        return MOE_OK;
-    }
-    if (events == nullptr) return fail(MOE_ERR_NULL, "events is NULL with n = %d", n);
-    if (n != MOE_STAGE_EVENTS) return fail(MOE_ERR_SHAPE, "n = %d, expected %d events", n, MOE_STAGE_EVENTS);
-    for (int i = 0; i < n; ++i)
-        if (events[i] == nullptr) return fail(MOE_ERR_NULL, "events[%d] is NULL", i);
-    for (int i = 0; i < n; ++i) g_stage_ev[i] = events[i];
-    g_stage_on = true;
     return MOE_OK;
 }
 

@@ -65,8 +65,11 @@ def _ws(lib, s):
     (dict(k=9, E=8), 2), (dict(E=257, k=2), 3), (dict(E=64, k=9), 3), (dict(H=60), 3),
     (dict(F=100), 3), (dict(dtype=7), 3), (dict(ffn=5), 3), (dict(flags=0x10), 3),
     (dict(capacity=-1), 2), (dict(T=1 << 31, k=1), 2), (dict(T=1 << 30, k=2), 2),
-    # 32-bit byte offsets of the grouped GEMM: an expert matrix or x of 4 GiB or more
+    # 32-bit byte offsets of the grouped GEMM with the out-of-range marker at 2^31: an
+    # expert matrix (plus 128 rows) or x of 2 GiB or more
     (dict(H=65536, F=32768), 3), (dict(H=8, F=1 << 24), 3), (dict(T=300000, H=8192), 3),
+    (dict(H=16384, F=65536), 3), (dict(T=131072, H=8192), 3),
+    (dict(H=8, F=(1 << 30) // 136 // 8 * 8 + 8), 3),
 ])
 def test_bad_shapes_are_rejected(lib, kw, code):
     s = _shape(**kw)
@@ -150,21 +153,61 @@ def test_workspace_grows_with_the_layer(lib):
     assert c - d < 256 * 256 * 256 * 4
 
 
-def test_capacity_rows():
+def test_largest_accepted_shapes(lib):
+    # just below the 2 GiB limits: (H + 128) * F * 2 bytes and T * H * 2 bytes
+    ok = _shape(H=8, F=(1 << 30) // 136 // 8 * 8)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == 0
+    ok2 = _shape(T=(1 << 30) // 8192 - 1, H=8192)
+    assert lib.moe_workspace_size(ctypes.byref(ok2), ctypes.byref(n)) == 0
+
+
+def test_capacity_rows(lib):
+    # the library's C = max(1, ceil(cf * T * k / E)) ([Principles §4.3], pairs as the total)
     assert _lib.capacity_rows(None, 8192, 2, 64) == 0
     assert _lib.capacity_rows(1.0, 8192, 2, 64) == 256
     assert _lib.capacity_rows(1.25, 8192, 2, 64) == 320
+    assert _lib.capacity_rows(0.75, 30, 2, 4) == 12            # ceil(11.25)
+    assert _lib.capacity_rows(1e-9, 1, 1, 256) == 1
+    rows = ctypes.c_int32(-5)
+    assert lib.moe_capacity_rows(0.0, 8, 2, 4, ctypes.byref(rows)) == 2
+    assert lib.moe_capacity_rows(float("nan"), 8, 2, 4, ctypes.byref(rows)) == 2
+    assert lib.moe_capacity_rows(1.0, 8, 0, 4, ctypes.byref(rows)) == 2
+    assert lib.moe_capacity_rows(1.0, 8, 2, 4, None) == 1
+    assert lib.moe_capacity_rows(1.0, 8, 2, 4, ctypes.byref(rows)) == 0 and rows.value == 4
 
 
-def test_stage_events_argument_checks(lib):
-    arr = (ctypes.c_void_p * 6)(*([FAKE] * 6))
-    assert lib.moe_set_stage_events(None, 6) == 1                 # NULL array
-    assert lib.moe_set_stage_events(arr, 5) == 2                  # wrong count
+def test_workspace_layout(lib):
+    for kw in (dict(), dict(T=1024), dict(T=1024, dtype=_lib.MOE_F32), dict(T=0)):
+        s = _shape(**kw)
+        lay = _lib.workspace_layout(_lib.Shape(**{f: getattr(s, f) for f, _ in _lib.MoeShape._fields_}))
+        assert lay["total"] == _ws(lib, s)
+        P, E = s.T * s.k, s.E
+        es = 4 if s.dtype == _lib.MOE_F32 else 2
+        spans = [("logit_parts", lay["logit_splits"] * s.T * E * 4), ("topk_idx", P * 4), ("topk_w", P * 4),
+                 ("counts", E * 4), ("offsets", (E + 1) * 4), ("sorted_token", P * 4),
+                 ("row_of_pair", P * 4), ("h", P * s.F * es), ("y", P * s.H * es)]
+        assert lay["logit_splits"] >= 1
+        ends = sorted((lay[n], lay[n] + b, n) for n, b in spans)
+        for (a0, a1, na), (b0, b1, nb) in zip(ends, ends[1:]):
+            assert a1 <= b0, (na, nb)                       # no overlap
+        assert all(lay[n] % 256 == 0 for n, _ in spans)
+        assert ends[-1][1] <= lay["total"]
+    assert lib.moe_workspace_layout(ctypes.byref(_shape()), None) == 1
+    assert lib.moe_workspace_layout(ctypes.byref(_shape(E=0)), ctypes.byref(_lib.MoeWorkspaceParts())) == 2
+
+
+def test_forward_timed_argument_checks(lib):
+    s = _shape()
+    ws = _ws(lib, s)
+    args = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws]
     bad = (ctypes.c_void_p * 6)(*([FAKE] * 5 + [None]))
-    assert lib.moe_set_stage_events(bad, 6) == 1                  # NULL entry
+    assert lib.moe_forward_timed(ctypes.byref(s), *args, bad, None) == 1          # NULL entry
     assert b"events[5]" in lib.moe_last_error()
-    assert lib.moe_set_stage_events(arr, 6) == 0                  # stored, nothing recorded yet
-    assert lib.moe_set_stage_events(None, 0) == 0                 # and switched off again
+    s0 = _shape(T=0)
+    arr = (ctypes.c_void_p * 6)(*([FAKE] * 6))
+    assert lib.moe_forward_timed(ctypes.byref(s0), *args[:-1], _ws(lib, s0), arr, None) == 0
+    assert lib.moe_forward_timed(ctypes.byref(s0), *args[:-1], _ws(lib, s0), None, None) == 0
 
 
 def test_peak_entry_points_argument_checks(lib):

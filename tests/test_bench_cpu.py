@@ -27,10 +27,14 @@ def test_worked_shape_algorithmic_work_by_hand():
     T, H, E, k, F = 8192, 4096, 64, 2, 16384
     P = T * k
     sb = A.stage_bytes(T, H, E, k, F, "silu2", "bf16", touched=64)
-    # first projection: every expert's W1 once, x once, h written once
-    assert sb.ffn_up == 64 * 4096 * 16384 * 2 + 8192 * 4096 * 2 + 16384 * 16384 * 2 == 9193914368
-    # second: every W2 once, h read once, the y rows written once
-    assert sb.ffn_down == 64 * 16384 * 4096 * 2 + 16384 * 16384 * 2 + 16384 * 4096 * 2
+    # algorithmic: the first projection every expert's W1 once and x once, the second
+    # every W2 once and out once
+    assert sb.ffn_up == 64 * 4096 * 16384 * 2 + 8192 * 4096 * 2 == 8657043456
+    assert sb.ffn_down == 64 * 16384 * 4096 * 2 + 8192 * 4096 * 2
+    assert sb.ffn_up + sb.ffn_down == sb.layer
+    # as designed: + h written once; + h read once and the y rows written once
+    assert sb.ffn_up_designed == sb.ffn_up + 16384 * 16384 * 2 == 9193914368
+    assert sb.ffn_down_designed == 64 * 16384 * 4096 * 2 + 16384 * 16384 * 2 + 16384 * 4096 * 2
     # 2 flops per multiply-add, one matrix each way
     assert A.ffn_up_flops(T, k, H, F, "silu2") == 2 * P * H * F == 2199023255552
     assert A.ffn_down_flops(T, k, H, F) == 2 * P * F * H
