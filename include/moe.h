@@ -191,6 +191,21 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
                        const void* w_out, void* out, void* workspace, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, layouts and results as moe_forward; the intermediates
+ * live in a static device scratch array of MOE_NOALLOC_SCRATCH_BYTES (256 MiB) inside
+ * the library, one per GPU, held until the process ends.  Nothing is allocated or
+ * freed by the call.  A layer whose moe_workspace_size() exceeds the scratch returns
+ * MOE_ERR_WORKSPACE (enqueuing nothing).  Every call on one GPU uses that GPU's one
+ * scratch array, so calls that overlap on a GPU (concurrent streams or threads) race
+ * and give undefined results: serialise them.  The call itself clears what its kernels
+ * need zeroed; nothing depends on an earlier call's contents. */
+#define MOE_NOALLOC_SCRATCH_BYTES (256u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_gate,
+                               const float* bias, const void* w_in, const void* w_up,
+                               const void* w_out, void* out, hipStream_t stream);
+
 /* Router statistics of one batch ([Principles §4.2, §5.2]), from fp32 logits (no bias)
  * and the per-expert counts:
  *   stats [E + 4] fp32 out: stats[e] = P_e, the mean over tokens of expert e's softmax

@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 
 EXPORTS = ["moe_workspace_size", "moe_workspace_layout", "moe_capacity_rows", "moe_route",
            "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
-           "moe_router_stats", "moe_status_str", "moe_last_error", "moe_peak_mfma_bf16",
+           "moe_forward_noalloc", "moe_router_stats", "moe_status_str", "moe_last_error",
+           "moe_peak_mfma_bf16",
            "moe_peak_hbm_read", "moe_peak_hbm_copy"]
 
 MOE_STAGE_EVENTS = 6
@@ -76,6 +77,7 @@ def load(path: str = LIB_PATH):
         "moe_combine": [sp, vp, i32p, f32p, vp, st],
         "moe_forward": [sp, vp, f32p, f32p, vp, vp, vp, vp, vp, ctypes.c_size_t, st],
         "moe_forward_timed": [sp, vp, f32p, f32p, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, st],
+        "moe_forward_noalloc": [sp, vp, f32p, f32p, vp, vp, vp, vp, st],
         "moe_router_stats": [sp, f32p, f32p, i32p, i32p, f32p, st],
     }
     for name, args in sig.items():
@@ -204,6 +206,17 @@ def forward(shape: Shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, st
     _check("moe_forward_timed", load().moe_forward_timed(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
                                                          _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
                                                          _ptr(workspace), nbytes, arr, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def forward_noalloc(shape: Shape, x, w_gate, bias, w_in, w_up, w_out, out, stream=None):
+    """moe_forward_noalloc: the layer with the library's static scratch (no workspace)."""
+    s = shape.c()
+    _check("moe_forward_noalloc", load().moe_forward_noalloc(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias),
+                                                             _ptr(w_in), _ptr(w_up), _ptr(w_out), _ptr(out),
+                                                             _stream(stream)))
 
 
 def router_stats(shape: Shape, logits, bias, counts, offsets, stats, stream=None):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -141,6 +142,22 @@ moe_status check_ws(const moe_shape& s, const void* ws, size_t ws_bytes) {
 }
 
 
+// Shape and pointer checks of the whole-layer entry points.
+moe_status check_forward_args(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                              const void* w_in, const void* w_up, const void* w_out, const void* out) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    REQ(x, "x");
+    REQ(w_gate, "w_gate");
+    OPT(bias, "bias");
+    REQ(w_in, "w_in");
+    REQ(w_out, "w_out");
+    REQ(out, "out");
+    if (shape->ffn == MOE_FFN_SWIGLU) REQ(w_up, "w_up");
+    else if (w_up) return fail(MOE_ERR_SHAPE, "w_up must be NULL for the SiLU two-layer FFN");
+    return MOE_OK;
+}
+
 moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_rows,
                        const int32_t* offsets, const void* w_in, const void* w_up,
                        const void* w_out, void* y, void* ws, const hipEvent_t* ev,
@@ -168,6 +185,33 @@ moe_status run_grouped(const moe_shape& s, const void* a, const int32_t* gather_
     HIPCHK(launch_grouped_ffn_bf16(a, gather_rows ? s.T : 0, gather_rows, w_in, w_up, w_out, at<void>(ws, L.h), y, tiles,
                                    ntiles, max_tiles_for(P, s.E, std::min(bma, bmb)), cfg, s.H, s.F, swiglu, sb, ev, st),
            "grouped_ffn_bf16");
+    return MOE_OK;
+}
+
+// Scratch of moe_forward_noalloc: a file-scope device array (each GPU the library runs on
+// holds its own copy until the process ends).  Host code never uses the array's name as
+// an address (on the host it is only a stand-in): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+moe_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return MOE_OK;
 }
 
@@ -289,17 +333,9 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const int32_t
 moe_status moe_forward_timed(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
                              const void* w_in, const void* w_up, const void* w_out, void* out,
                              void* workspace, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream) {
-    moe_status st = check_shape(shape);
+    moe_status st = check_forward_args(shape, x, w_gate, bias, w_in, w_up, w_out, out);
     if (st != MOE_OK) return st;
     const moe_shape& s = *shape;
-    REQ(x, "x");
-    REQ(w_gate, "w_gate");
-    OPT(bias, "bias");
-    REQ(w_in, "w_in");
-    REQ(w_out, "w_out");
-    REQ(out, "out");
-    if (s.ffn == MOE_FFN_SWIGLU) REQ(w_up, "w_up");
-    else if (w_up) return fail(MOE_ERR_SHAPE, "w_up must be NULL for the SiLU two-layer FFN");
     if ((st = check_ws(s, workspace, ws_bytes)) != MOE_OK) return st;
     if (events)
         for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
@@ -338,6 +374,22 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
                        const void* w_in, const void* w_up, const void* w_out, void* out,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
     return moe_forward_timed(shape, x, w_gate, bias, w_in, w_up, w_out, out, workspace, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                               const void* w_in, const void* w_up, const void* w_out, void* out,
+                               hipStream_t stream) {
+    moe_status st = check_forward_args(shape, x, w_gate, bias, w_in, w_up, w_out, out);
+    if (st != MOE_OK) return st;
+    const size_t need = layout_of(*shape).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "this layer needs %zu bytes of scratch; the library's static scratch holds %zu "
+                    "(use moe_forward with a caller workspace)", need, kScratchBytes);
+    if (shape->T == 0) return MOE_OK;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+    return moe_forward_timed(shape, x, w_gate, bias, w_in, w_up, w_out, out, ws, kScratchBytes, nullptr, stream);
 }
 
 moe_status moe_workspace_layout(const moe_shape* shape, moe_workspace_parts* parts) {

@@ -224,3 +224,17 @@ def test_peak_entry_points_argument_checks(lib):
     assert lib.moe_peak_hbm_copy(FAKE, None, 1 << 20, 256, None) == 1
     assert lib.moe_peak_hbm_copy(FAKE, FAKE + (1 << 19), 1 << 20, 256, None) == 2   # overlap
     assert b"overlap" in lib.moe_last_error()
+
+
+def test_forward_noalloc_argument_checks(lib):
+    # refused on the host before any device work: too large for the static scratch,
+    # NULL or misaligned pointers, a bad shape; T == 0 is a no-op
+    big = _shape(T=8192, H=4096, E=64, k=2, F=16384, ffn=_lib.MOE_FFN_SILU2)
+    assert lib.moe_forward_noalloc(ctypes.byref(big), FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None) == 5
+    assert b"static scratch" in lib.moe_last_error()
+    s = _shape()
+    assert _ws(lib, s) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(s), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moe_forward_noalloc(ctypes.byref(s), FAKE, FAKE, MIS, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert lib.moe_forward_noalloc(ctypes.byref(_shape(E=0)), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.moe_forward_noalloc(ctypes.byref(_shape(T=0)), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 0
