@@ -325,7 +325,8 @@ __device__ __forceinline__ int wblk(int blk, int g) {
 // swa4(m) = (m >> 1) & 2 the 16 lanes of every cycle land on distinct bank quads.
 __device__ __forceinline__ int swa4(int m) { return (m >> 1) & 2; }
 
-constexpr uint32_t kOOB = 0x80000000u;          // an offset past every buffer: reads zeros
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kWStream = 2;                     // the nt bit of a buffer load's cache policy          // an offset past every buffer: reads zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -1131,8 +1132,9 @@ __device__ __forceinline__ void pp_dma_a(lds_char* dst, __amdgpu_buffer_rsrc_t r
     }
 }
 
-// This wavefront's share of the W DMA of K step kt into W stage `dst`.
-template <int BM, int NMAT, int GROUP>
+// This wavefront's share of the W DMA of K step kt into W stage `dst`, with cache policy
+// WAUX (kWStream: the non-temporal hint, for a slice that one work item reads).
+template <int BM, int NMAT, int GROUP, int WAUX>
 __device__ __forceinline__ void pp_dma_w(lds_char* dst, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
                                          const PpPlanOf<BM, NMAT, GROUP>& pl, int kt, uint32_t rowB, int wave) {
     using S = PpShape<BM, NMAT>;
@@ -1144,20 +1146,20 @@ __device__ __forceinline__ void pp_dma_w(lds_char* dst, __amdgpu_buffer_rsrc_t r
         const int j = j0 + i;
         const uint32_t off = pl.b_off[i] == kOOB ? kOOB : pl.b_off[i] + k0 * rowB;
         const __amdgpu_buffer_rsrc_t rb = (NMAT == 2 && j >= S::BMAT_DMA) ? rb1 : rb0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + j * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst + j * 1024), 16, off, 0, 0, WAUX);
     }
 }
 
 // One read phase's DMA: A of step r + NA - 1 and W of step r + NW - 1 (r relative to the
 // work's first step kt0), each into the stage its ring held for step r - 1.
-template <int BM, int NMAT, int GROUP>
+template <int BM, int NMAT, int GROUP, int WAUX>
 __device__ __forceinline__ void pp_dma_step(lds_char* lds, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
                                             __amdgpu_buffer_rsrc_t rb1, const PpPlanOf<BM, NMAT, GROUP>& pl,
                                             int kt0, int r, int K, uint32_t rowB, int wave) {
     using S = PpShape<BM, NMAT>;
     const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
     pp_dma_a<BM, NMAT, GROUP>(lds + (ra_step % S::NA) * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave);
-    pp_dma_w<BM, NMAT, GROUP>(lds + S::W_RING + (rw_step % S::NW) * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step,
+    pp_dma_w<BM, NMAT, GROUP, WAUX>(lds + S::W_RING + (rw_step % S::NW) * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step,
                               rowB, wave);
 }
 
@@ -1230,7 +1232,7 @@ __device__ __forceinline__ void pp_read(const lds_char* As, const lds_char* Bs, 
 // The K loop of one group (see the phase table above) over K steps kt0 .. kt0 + KT - 1.
 // `nblk`: the wavefront's 16-row blocks that hold rows of the tile (only they are
 // multiplied; with none the wavefront only moves its DMA share and keeps the barriers).
-template <int GROUP, int BM, int NMAT>
+template <int GROUP, int BM, int NMAT, int WAUX>
 __device__ __attribute__((always_inline)) inline void pp_kloop(
     lds_char* lds, int kt0, int KT, int nblk, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0,
     __amdgpu_buffer_rsrc_t rb1, const PpPlanOf<BM, NMAT, GROUP>& pl, int K, uint32_t rowB, int wave, int a_rd,
@@ -1245,7 +1247,7 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
         pp_read<BM, NMAT>(lds + (kt % S::NA) * S::A_STAGE, lds + S::W_RING + (kt % S::NW) * S::B_STAGE, a_rd, b_rd,
                           g, wn, af, bfr);
         __builtin_amdgcn_sched_barrier(0);
-        pp_dma_step<BM, NMAT, GROUP>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
+        pp_dma_step<BM, NMAT, GROUP, WAUX>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if constexpr (GROUP == 1) wait_vmcnt<VMCNT>();           // step kt + 1 complete
         kloop_barrier();
@@ -1272,8 +1274,9 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
 
 // The whole K loop of one work item for group GROUP: plan, prologue, loop.  The prologue
 // issues the DMA as the steps -(NW - 1) .. -1 would have (A of steps below 0 as zero
-// placeholders), so the first steps wait with the same count as the rest.
-template <int GROUP, int BM, int NMAT, bool GATHER>
+// placeholders), so the first steps wait with the same count as the rest.  WAUX: the
+// cache policy of the W loads.
+template <int GROUP, int BM, int NMAT, bool GATHER, int WAUX>
 __device__ __attribute__((always_inline)) inline void pp_item(
     lds_char* lds, int kt0, int KT, int nblk, const Tile& tl, int rows, int n0, int K, int N,
     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb0, __amdgpu_buffer_rsrc_t rb1,
@@ -1288,11 +1291,11 @@ __device__ __attribute__((always_inline)) inline void pp_item(
         const int ra_step = r + S::NA - 1, rw_step = r + S::NW - 1;
         const int aslot = ((ra_step % S::NA) + S::NA) % S::NA;
         pp_dma_a<BM, NMAT, GROUP>(lds + aslot * S::A_STAGE, ra, pl, kt0 + ra_step, K, wave, ra_step < 0);
-        pp_dma_w<BM, NMAT, GROUP>(lds + S::W_RING + rw_step * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
+        pp_dma_w<BM, NMAT, GROUP, WAUX>(lds + S::W_RING + rw_step * S::B_STAGE, rb0, rb1, pl, kt0 + rw_step, rowB, wave);
     }
     wait_vmcnt<S::template vmcnt<GROUP>()>();                    // step 0 complete for all
     kloop_barrier();
-    pp_kloop<GROUP, BM, NMAT>(lds, kt0, KT, nblk, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
+    pp_kloop<GROUP, BM, NMAT, WAUX>(lds, kt0, KT, nblk, ra, rb0, rb1, pl, K, rowB, wave, a_rd, b_rd, g, wn, acc);
 }
 
 // Output of one ping-pong work item: block(fm, fn) gives this wavefront's fp32 sums for
@@ -1443,12 +1446,21 @@ __device__ __forceinline__ void gemm_tiles_pp(
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        if (grp == 0)
-            pp_item<0, BM, NMAT, GATHER>(lds, kt0, nsteps, nblk, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
-                                         wave, lane, a_rd, b_rd, g, wn, acc);
-        else
-            pp_item<1, BM, NMAT, GATHER>(lds, kt0, nsteps, nblk, tl, rows, n0, K, N, ra, rb0, rb1, gather_rows,
-                                         wave, lane, a_rd, b_rd, g, wn, acc);
+        // An expert held by one row tile has each of its weight slices read by one work
+        // item only: those loads carry the non-temporal hint, so the one-pass weight
+        // stream of the many short experts leaves L2 before the row tiles and weight
+        // slices that the items of the long experts share.
+        const bool wstream = tl.cnt == 1;
+#define MOE_PP_ITEM(G_, AUX_) pp_item<G_, BM, NMAT, GATHER, AUX_>(lds, kt0, nsteps, nblk, tl, rows, n0, K, N, ra, rb0, \
+                                                              rb1, gather_rows, wave, lane, a_rd, b_rd, g, wn, acc)
+        if (grp == 0) {
+            if (wstream) MOE_PP_ITEM(0, kWStream);
+            else MOE_PP_ITEM(0, 0);
+        } else {
+            if (wstream) MOE_PP_ITEM(1, kWStream);
+            else MOE_PP_ITEM(1, 0);
+        }
+#undef MOE_PP_ITEM
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
         __syncthreads();
 

@@ -9,8 +9,8 @@
 // ([T, H] x [H, E], E <= 256).  For fp32 x, and for short batches, it runs on the fp32
 // MFMA (v_mfma_f32_16x16x4_f32): exact widening of bf16 x, fp32 products and
 // accumulation.  For bf16 x it runs on the bf16 MFMA with the weights split exactly
-// into three bf16 parts (k_gate_logits_x3): the same fp32 products and accumulation.  Top-k is one wavefront per
-// token: each lane holds up to four experts, k rounds of a wave-wide arg-max pick
+// into three bf16 parts (k_gate_logits_x3): the same fp32 products and accumulation.
+// Top-k is one wavefront per token: each lane holds up to four experts, k rounds of a wave-wide arg-max pick
 // the winners ([FourStage §2.2]); gates are the softmax over the chosen logits,
 // which equals the full softmax renormalised over the k chosen ([Principles §2.2]).
 #include "common.h"
@@ -142,10 +142,6 @@ __global__ __launch_bounds__(256) void k_gate_logits(const XT* __restrict__ x,
 // products and accumulation as the fp32 MFMA, at 3 x 16 instead of 8 x 32 cycles per
 // 32 of K.  (Outside the exact range: weights above about 3.39e38, whose bf16 rounding
 // is infinite, and below about 2^-110, whose third part loses low bits.)
-// Tile: TM tokens x 64 experts per workgroup, K in steps of 64 over this workgroup's K
-// range (split-K as in k_gate_logits).  Wave w owns expert columns [16w, 16w + 16).
-// x stays row-major in LDS, the split weights are stored expert-major (k contiguous), so
-// both MFMA operands are single 16-byte LDS reads.
 __device__ __forceinline__ void split3_bf16(float w, float& h, float& m, float& l) {
     h = (float)(__bf16)w;
     const float r = w - h;
@@ -155,125 +151,132 @@ __device__ __forceinline__ void split3_bf16(float w, float& h, float& m, float& 
 
 constexpr int GX_PITCH = GT_K + 8;          // bf16 per LDS row (16-byte pad)
 
-template <int TM>
-__global__ __launch_bounds__(256) void k_gate_logits_x3(const bf16_t* __restrict__ x,
-                                                        const float* __restrict__ wg,
-                                                        float* __restrict__ out, int T, int H, int E,
-                                                        int kchunk) {
+// Tile: 256 tokens x TE experts per workgroup of 8 wavefronts (TE = 128 when E > 64,
+// else 64), K in steps of 64 over this workgroup's K range (split-K as in k_gate_logits).
+// The wavefronts form a 4 x 2 grid: wavefront (wm, wn) owns tokens [64 wm, 64 wm + 64)
+// and experts [wn TE/2, (wn + 1) TE/2), i.e. 4 x TE/32 blocks of 16 x 16 fp32
+// accumulators, two wavefronts per SIMD so that one's LDS reads overlap the other's
+// MFMAs.  Against a 128-token x 64-expert tile this reads W_g half as often (once per 256
+// tokens), and x half as often when E > 64 (once per 128 experts).  The next step's x and
+// W_g travel into registers while the current step's MFMAs run from LDS.
+template <int TE>
+__global__ __launch_bounds__(512, 1) void k_gate_logits_x3(const bf16_t* __restrict__ x,
+                                                           const float* __restrict__ wg,
+                                                           float* __restrict__ out, int T, int H, int E,
+                                                           int kchunk) {
+    constexpr int TM = 256;
+    constexpr int NB = TE / 32;                 // 16-expert column blocks per wavefront
+    constexpr int FM = 4;                       // 16-token row blocks per wavefront
+    constexpr int NPAIR = 16 * (TE / 4);        // (k quad, expert quad) pairs of one W step
     __shared__ __attribute__((aligned(16))) bf16_t sX[TM][GX_PITCH];
-    __shared__ __attribute__((aligned(16))) bf16_t sW[3][GT_E][GX_PITCH];
+    __shared__ __attribute__((aligned(16))) bf16_t sW[3][TE][GX_PITCH];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int m0 = blockIdx.x * TM, e0 = blockIdx.y * GT_E;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
     const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
-    constexpr int FM = TM / 16;
-    // x loader: TM rows x 8 chunks of 8 bf16 per step; thread -> (row, XCH chunks)
-    constexpr int XCH = TM * 8 / 256 > 0 ? TM * 8 / 256 : 1;
-    constexpr bool XPART = TM * 8 < 256;
-    const int xrow = tid / (8 / XCH), xc0 = (tid % (8 / XCH)) * XCH;
-    // W loader: thread -> k rows 4 kq .. 4 kq + 3, experts 4 eg .. 4 eg + 3
-    const int kq = tid & 15, eg = tid >> 4;
-    // one K step's operands in registers; two are in flight (the loads of step k + 2 are
-    // issued before step k's MFMAs), which covers HBM latency for x
-    struct Stage {
-        uint4 xr[XCH];
-        float4 wr[4];
-    };
-    auto gload = [&](Stage& sg, int k0) {
+    // x loader: load i of thread t moves 16 bytes (8 k) of row (t >> 3) + 64 i, chunk t & 7,
+    // so the 8 lanes of one row read its 128 bytes of the step together
+    const int xr0 = tid >> 3, xc = tid & 7;
+    // W loader: thread t < NPAIR takes expert quad eg = t % (TE/4) and k quad kq = t / (TE/4):
+    // four float4 rows of 4 experts, so each expert's 4 k values pack into one 8-byte LDS
+    // store per plane
+    const bool wthr = tid < NPAIR;
+    const int eg = tid % (TE / 4), kq = tid / (TE / 4);
+    uint4 xr[4];
+    float4 wr[4];
+    auto gload = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < XCH; ++j) {
-            const int t = m0 + xrow, kk = k0 + 8 * (xc0 + j);
-            sg.xr[j] = make_uint4(0u, 0u, 0u, 0u);
-            if ((!XPART || tid < TM * 8) && t < T && kk < kend)
-                sg.xr[j] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+        for (int i = 0; i < 4; ++i) {
+            const int t = m0 + xr0 + 64 * i, kk = k0 + 8 * xc;
+            xr[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (t < T && kk < kend) xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
         }
+        const int e = e0 + 4 * eg;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kk = k0 + 4 * kq + j, e = e0 + 4 * eg;
-            sg.wr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kk < kend) {
+        for (int r = 0; r < 4; ++r) {
+            const int kk = k0 + 4 * kq + r;
+            wr[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (wthr && kk < kend) {
                 if (e + 3 < E) {
-                    sg.wr[j] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
+                    wr[r] = *reinterpret_cast<const float4*>(wg + (size_t)kk * E + e);
                 } else {
                     float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = (e + i < E) ? wg[(size_t)kk * E + e + i] : 0.f;
-                    sg.wr[j] = make_float4(v[0], v[1], v[2], v[3]);
+                    for (int c = 0; c < 4; ++c) v[c] = (e + c < E) ? wg[(size_t)kk * E + e + c] : 0.f;
+                    wr[r] = make_float4(v[0], v[1], v[2], v[3]);
                 }
             }
         }
     };
-    auto lstore = [&](const Stage& sg) {
-        if (!XPART || tid < TM * 8) {
+    auto lstore = [&]() {
 #pragma unroll
-            for (int j = 0; j < XCH; ++j) *reinterpret_cast<uint4*>(&sX[xrow][8 * (xc0 + j)]) = sg.xr[j];
-        }
-        // expert i of this thread: its 4 k values, split into the three bf16 planes
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sX[xr0 + 64 * i][8 * xc]) = xr[i];
+        if (wthr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4* wr = sg.wr;
-            const float w4[4] = {i == 0 ? wr[0].x : i == 1 ? wr[0].y : i == 2 ? wr[0].z : wr[0].w,
-                                 i == 0 ? wr[1].x : i == 1 ? wr[1].y : i == 2 ? wr[1].z : wr[1].w,
-                                 i == 0 ? wr[2].x : i == 1 ? wr[2].y : i == 2 ? wr[2].z : wr[2].w,
-                                 i == 0 ? wr[3].x : i == 1 ? wr[3].y : i == 2 ? wr[3].z : wr[3].w};
-            float h[4], m[4], l[4];
+            for (int c = 0; c < 4; ++c) {      // expert 4 eg + c: its 4 k values, split in 3 planes
+                float h[4], m[4], l[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) split3_bf16(w4[j], h[j], m[j], l[j]);
-            const int e = 4 * eg + i;
-            *reinterpret_cast<uint2*>(&sW[0][e][4 * kq]) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            *reinterpret_cast<uint2*>(&sW[1][e][4 * kq]) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
-            *reinterpret_cast<uint2*>(&sW[2][e][4 * kq]) = make_uint2(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]));
-        }
-    };
-    f32x4_t acc[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int fr = lane & 15, fq = lane >> 4;
-    auto mfma_step = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < GT_K; ks += 32) {
-            bf16x8_t b[3];
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-                b[p] = *reinterpret_cast<const bf16x8_t*>(&sW[p][16 * wave + fr][ks + 8 * fq]);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sX[16 * fm + fr][ks + 8 * fq]);
-                // the small parts first
-                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[2], acc[fm], 0, 0, 0);
-                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[1], acc[fm], 0, 0, 0);
-                acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[0], acc[fm], 0, 0, 0);
+                for (int r = 0; r < 4; ++r) {
+                    const float4& v = wr[r];
+                    split3_bf16(c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w, h[r], m[r], l[r]);
+                }
+                const int e = 4 * eg + c;
+                *reinterpret_cast<uint2*>(&sW[0][e][4 * kq]) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                *reinterpret_cast<uint2*>(&sW[1][e][4 * kq]) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
+                *reinterpret_cast<uint2*>(&sW[2][e][4 * kq]) = make_uint2(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]));
             }
         }
     };
+    f32x4_t acc[FM][NB];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int fr = lane & 15, fq = lane >> 4;
     if (kbeg < kend) {
-        Stage s0, s1;
-        gload(s0, kbeg);
-        gload(s1, kbeg + GT_K);                 // (past kend: zeros, no loads)
-        for (int k0 = kbeg; k0 < kend; k0 += 2 * GT_K) {
+        gload(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
             __syncthreads();
-            lstore(s0);
+            lstore();
             __syncthreads();
-            gload(s0, k0 + 2 * GT_K);
-            mfma_step();
-            if (k0 + GT_K >= kend) break;
-            __syncthreads();
-            lstore(s1);
-            __syncthreads();
-            gload(s1, k0 + 3 * GT_K);
-            mfma_step();
+            if (k0 + GT_K < kend) gload(k0 + GT_K);
+#pragma unroll
+            for (int ks = 0; ks < GT_K; ks += 32) {
+                bf16x8_t b[NB][3], a[FM];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        b[nb][p] = *reinterpret_cast<const bf16x8_t*>(
+                            &sW[p][wn * (TE / 2) + 16 * nb + fr][ks + 8 * fq]);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    a[fm] = *reinterpret_cast<const bf16x8_t*>(&sX[64 * wm + 16 * fm + fr][ks + 8 * fq]);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        // the small parts first
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
+                    }
+            }
         }
     }
     // 16x16 block: lane holds column (lane & 15), rows 4*(lane >> 4) + v.
     float* o = out + (size_t)blockIdx.z * T * E;
-    const int e = e0 + wave * 16 + (lane & 15);
-    if (e < E) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int e = e0 + wn * (TE / 2) + 16 * nb + fr;
+        if (e >= E) continue;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = m0 + fm * 16 + 4 * (lane >> 4) + v;
-                if (t < T) o[(size_t)t * E + e] = acc[fm][v];
+                const int t = m0 + 64 * wm + fm * 16 + 4 * fq + v;
+                if (t < T) o[(size_t)t * E + e] = acc[fm][nb][v];
             }
     }
 }
@@ -401,16 +404,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 // -------------------------------------------------------------------- launchers
-// Row-tile height of the gate projection: 16 tokens for short batches (fp32 MFMA), else
-// 128 for bf16 x (split weights, whose conversion each workgroup repeats: taller tiles
-// amortise it) and 64 for fp32 x.
-int gate_tile_rows(long long T, int dtype) { return T <= 256 ? 16 : (dtype == MOE_F32 ? 64 : 128); }
+// Tile of the gate projection: 16 tokens for short batches (fp32 MFMA), 64 for fp32 x,
+// and 256 tokens x 64 or 128 experts for bf16 x (split weights, 512 threads).
+int gate_tile_rows(long long T, int dtype) { return T <= 256 ? 16 : (dtype == MOE_F32 ? 64 : 256); }
+int gate_tile_experts(long long T, int E, int dtype) {
+    return (T > 256 && dtype != MOE_F32 && E > 64) ? 128 : GT_E;
+}
 
+// K ranges of the gate projection: enough workgroups for the CUs.  The bf16 tiles hold one
+// workgroup per CU (92 KB of LDS), so they aim at 256 workgroups; the fp32 tiles at 512.
 int gate_splits(long long T, int H, int E, int dtype) {
     if (T <= 0) return 1;
-    const long long tm = gate_tile_rows(T, dtype);
-    const long long base = ((T + tm - 1) / tm) * ((E + GT_E - 1) / GT_E);
-    long long sp = (512 + base - 1) / base;
+    const long long tm = gate_tile_rows(T, dtype), te = gate_tile_experts(T, E, dtype);
+    const long long base = ((T + tm - 1) / tm) * ((E + te - 1) / te);
+    const long long aim = tm == 256 ? 256 : 512;
+    long long sp = (aim + base - 1) / base;
     const long long maxs = (H + 255) / 256;
     if (sp > maxs) sp = maxs;
     return (int)(sp < 1 ? 1 : sp);
@@ -431,8 +439,13 @@ hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* 
         const dim3 grid((unsigned)((T + 63) / 64), gy, (unsigned)splits);
         hipLaunchKernelGGL((k_gate_logits<64, float>), grid, blk, 0, st, (const float*)x, wg, out, (int)T, H, E, kchunk);
     } else {
-        const dim3 grid((unsigned)((T + 127) / 128), gy, (unsigned)splits);
-        hipLaunchKernelGGL((k_gate_logits_x3<128>), grid, blk, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
+        const int te = gate_tile_experts(T, E, dtype);
+        const dim3 grid((unsigned)((T + 255) / 256), (unsigned)((E + te - 1) / te), (unsigned)splits);
+        const dim3 blk2(512);
+        if (te == 128)
+            hipLaunchKernelGGL((k_gate_logits_x3<128>), grid, blk2, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
+        else
+            hipLaunchKernelGGL((k_gate_logits_x3<64>), grid, blk2, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
     }
     return hipGetLastError();
 }
