@@ -1364,6 +1364,212 @@ __device__ __attribute__((noinline)) void pp_write_split(lds_char* lds, __amdgpu
     pp_write_out<BM, NMAT, ACT>(lds, block, nblk, row0, wn, l16, lq, tid, rows, n0, N, C_rows);
 }
 
+// ------------------------------------------ thin row tiles inside the ping-pong kernel
+// A row tile of at most 64 rows (an expert with few rows, or the ragged last tile of a
+// long one) does little MFMA work: its cost is streaming its weight slice.  The ping-pong
+// K loop would spend on it what it spends on a full tile: two phases and four barriers
+// per K step, every wavefront reading all its fragments, and 16 A loads per step of which
+// most only write zeros.  Such a tile instead runs this loop: one barrier per K step, an
+// A stage of 64 rows (4 loads), both operands in rings of ThinShape::NS stages with the
+// DMA LEAD steps ahead (more weight bytes in flight per CU), and each wavefront
+// multiplying only the 16-row blocks that hold rows, for its own output columns: 16 of
+// them (gate and up) for SwiGLU, else 32.  The LDS layouts and swizzles are those of the
+// 256-row tile (W rows of 256 columns, A rows of 64 bytes), so the fragment reads are the
+// ping-pong kernel's.
+template <int NMAT>
+struct ThinShape {
+    using P = PpShape<256, NMAT>;
+    static constexpr int BK = 32, ROWS = 64;
+    static constexpr int A_STAGE = ROWS * BK * 2;           // 4 KB
+    static constexpr int B_STAGE = P::B_STAGE;              // 16 KB: 32 rows x 256 columns
+    static constexpr int NS = 8, LEAD = NS - 1;             // stages per operand, DMA lead
+    static constexpr int W_RING = 0, A_RING = NS * B_STAGE;
+    static constexpr int AINSTR = A_STAGE / 1024;           // A loads per step: wavefronts 0-3
+    static constexpr int BINSTR = B_STAGE / 1024;           // W loads per step: 2 per wavefront
+    static constexpr int RING_BYTES = NS * (A_STAGE + B_STAGE);
+    static_assert(RING_BYTES <= 160 * 1024, "the thin rings fit the LDS");
+    static_assert(BINSTR == 16 && AINSTR == 4, "wavefront w loads W pieces 2w, 2w + 1 and A piece w < 4");
+    static_assert((LEAD - 1) * 3 < 64, "DMA in flight fits the 6-bit vmcnt");
+};
+
+// LDS of a ping-pong launch: its rings (or the output staging tile) and the thin tiles' rings.
+template <int BM, int NMAT>
+constexpr size_t pp_lds_bytes() {
+    return BM == 256 && (size_t)ThinShape<NMAT>::RING_BYTES > PpShape<BM, NMAT>::LDS_BYTES
+               ? (size_t)ThinShape<NMAT>::RING_BYTES
+               : PpShape<BM, NMAT>::LDS_BYTES;
+}
+
+// One K step of a thin tile: the DMA of step s + LEAD into the stages `dA` / `dB` (those
+// of step s - 1), then this step's fragments from `As` / `Bs` and its MFMAs.  The stages
+// are distinct, and saying so with __restrict__ lets the compiler issue the fragment reads
+// without waiting for the DMA in flight.
+template <int NMAT, int WAUX>
+__device__ __attribute__((always_inline)) inline void thin_step(
+    const lds_char* __restrict__ As, const lds_char* __restrict__ Bs, lds_char* __restrict__ dA,
+    lds_char* __restrict__ dB, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t a_off, uint32_t a_k,
+    const uint32_t (&b_off)[2], uint32_t k0, int K, uint32_t rowB, int wave, int a_rd, int b_rd, int g, int blk0,
+    int mat1, int blk1, int fmt, f32x4_t (&acc)[4][2]) {
+    using S = ThinShape<NMAT>;
+    using P = PpShape<256, NMAT>;
+    constexpr int BK = S::BK, BROW = P::BROW;
+    if (wave < S::AINSTR) {
+        const uint32_t off = (k0 + a_k < (uint32_t)K) ? a_off + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dA + wave * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t off = (k0 >= (uint32_t)K || b_off[i] == kOOB) ? kOOB : b_off[i] + k0 * rowB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dB + (2 * wave + i) * 1024), 16, off, 0, 0, WAUX);
+    }
+    auto read_b = [&](int mat, int blk) -> bf16x8_t {
+        const lds_char* p = Bs + mat * BK * BROW + b_rd + (wblk<256, NMAT>(blk, g) << 5);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * BROW));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
+    const bf16x8_t b0 = read_b(0, blk0), b1 = read_b(mat1, blk1);
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+        if (fm < fmt) {
+            const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(As + a_rd + fm * 16 * BK * 2);
+            acc[fm][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[fm][0], 0, 0, 0);
+            acc[fm][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[fm][1], 0, 0, 0);
+        }
+    }
+}
+
+// The whole thin tile: plan, prologue, K loop, epilogue.  Every value that selects memory
+// (the tile, the operand resources) is wavefront-uniform and kept in scalar registers.
+template <int NMAT, int ACT, bool GATHER, int WAUX>
+__device__ __attribute__((always_inline)) inline void pp_thin_item(
+    lds_char* lds, const bf16_t* __restrict__ A, long long a_rows, const int32_t* __restrict__ gather_rows,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int e, int row0, int rows,
+    int n0, int K, int N) {
+    using S = ThinShape<NMAT>;
+    using P = PpShape<256, NMAT>;
+    constexpr int BK = S::BK, BROW = P::BROW, BNm = P::BNm, CS_STRIDE = P::CS_STRIDE, NS = S::NS, LEAD = S::LEAD;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int KT = (K + BK - 1) / BK;
+    const uint32_t rowB = (uint32_t)N * 2;
+    const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, (uint32_t)(a_rows * K * 2))
+                                             : make_rsrc(A + (long long)row0 * K, (uint32_t)rows * K * 2);
+    const long long eoff = (long long)e * K * N;
+    // W piece j = 2 wave + i; SwiGLU's pieces 8..15 are the up matrix's
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc((NMAT == 2 && wave >= 4 ? B1 : B0) + eoff, (uint32_t)K * rowB);
+    // A piece `wave` (wavefronts 0-3): rows 16 wave .. 16 wave + 15, four 16-byte chunks each
+    uint32_t a_off = kOOB, a_k = 0;
+    if (wave < S::AINSTR) {
+        const int r = wave * 16 + (lane >> 2);
+        const int q = (lane & 3) ^ swa4(r);
+        a_k = (uint32_t)(q * 8);
+        long long row = row0 + min(r, rows - 1);
+        if constexpr (GATHER) row = gather_rows[row];
+        else row -= row0;
+        a_off = r < rows ? (uint32_t)(row * K * 2) + (uint32_t)(q * 16) : kOOB;
+    }
+    // W pieces, placed as in the 256-row tile
+    uint32_t b_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = 2 * wave + i;
+        int k, c;
+        if constexpr (NMAT == 1) {
+            k = j * 2 + (lane >> 5);
+            c = (lane & 31) ^ fk(k);
+        } else {
+            k = (j & 7) * 4 + (lane >> 4);
+            c = (lane & 15) ^ fk(k);
+        }
+        const uint32_t col = (uint32_t)(n0 + 8 * c);
+        b_off[i] = (8 * c < BNm && col < (uint32_t)N) ? (uint32_t)k * rowB + col * 2 : kOOB;
+    }
+    // fragment reads (the ping-pong kernel's addressing for the 256-row tile)
+    const int a_rd = l16 * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+    const int g = ((l16 >> 2) & 3) | ((lq & 1) << 2);
+    const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
+    // this wavefront's two column blocks: SwiGLU gate / up block `wave`, else blocks 2 wave, 2 wave + 1
+    const int mat1 = NMAT == 2 ? 1 : 0;
+    const int blk0 = NMAT == 2 ? wave : 2 * wave, blk1 = NMAT == 2 ? wave : 2 * wave + 1;
+    const int fmt = __builtin_amdgcn_readfirstlane((rows + 15) / 16);   // row blocks holding rows (1..4)
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // prologue: the DMA of steps 0 .. LEAD - 1 into stages 0 .. LEAD - 1
+#pragma unroll
+    for (int s = 0; s < LEAD; ++s) {
+        const uint32_t k0 = (uint32_t)s * BK;
+        if (wave < S::AINSTR) {
+            const uint32_t off = (k0 + a_k < (uint32_t)K) ? a_off + k0 * 2 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void*)(lds + S::A_RING + s * S::A_STAGE + wave * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t off = (k0 >= (uint32_t)K || b_off[i] == kOOB) ? kOOB : b_off[i] + k0 * rowB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void*)(lds + S::W_RING + s * S::B_STAGE + (2 * wave + i) * 1024), 16, off, 0, 0, WAUX);
+        }
+    }
+    for (int s = 0; s < KT; ++s) {
+        // this wavefront's DMA of step s has landed (LEAD - 1 later steps may be in flight),
+        // and its fragment reads of step s - 1 are done; after the barrier both hold for all
+        if (wave < S::AINSTR) wait_vmcnt<(LEAD - 1) * 3>();
+        else wait_vmcnt<(LEAD - 1) * 2>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        kloop_barrier();
+        const int cur = s % NS, nxt = (s + LEAD) % NS;       // nxt: the stage step s - 1 used
+        thin_step<NMAT, WAUX>(lds + S::A_RING + cur * S::A_STAGE, lds + S::W_RING + cur * S::B_STAGE,
+                              lds + S::A_RING + nxt * S::A_STAGE, lds + S::W_RING + nxt * S::B_STAGE, ra, rb,
+                              a_off, a_k, b_off, (uint32_t)(s + LEAD) * BK, K, rowB, wave, a_rd, b_rd, g, blk0, mat1,
+                              blk1, fmt, acc);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the zero loads past K land before LDS is reused
+    __syncthreads();
+    // epilogue: activation, one rounding to bf16, staged in LDS, written as 16-byte row pieces
+    typedef __attribute__((address_space(3))) bf16_t lds_bf16;
+    lds_bf16* sC = reinterpret_cast<lds_bf16*>(lds);
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+        if (fm >= fmt) break;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * fm + 4 * lq + v;
+            if constexpr (NMAT == 2) {
+                sC[r * CS_STRIDE + 16 * wave + l16] = f32_to_bf16(silu_f32(acc[fm][0][v]) * acc[fm][1][v]);
+            } else {
+                float v0 = acc[fm][0][v], v1 = acc[fm][1][v];
+                if constexpr (ACT == 1) {
+                    v0 = silu_f32(v0);
+                    v1 = silu_f32(v1);
+                }
+                sC[r * CS_STRIDE + 32 * wave + l16] = f32_to_bf16(v0);
+                sC[r * CS_STRIDE + 32 * wave + 16 + l16] = f32_to_bf16(v1);
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int CPR = BNm / 8;
+    bf16_t* C_rows = C + (long long)row0 * N;
+    for (int c = tid; c < rows * CPR; c += 512) {
+        const int r = c / CPR, cc = c % CPR;
+        const int col = n0 + cc * 8;
+        if (col < N)
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(sC + r * CS_STRIDE + cc * 8),
+                reinterpret_cast<u32x4_t*>(C_rows + (long long)r * N + col));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
 // All work items of one launch, ping-pong form.  part_buf / part_cnt as for gemm_tiles
 // (the split of the last round), used by the SPLIT instance only.
 template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
@@ -1420,6 +1626,17 @@ __device__ __forceinline__ void gemm_tiles_pp(
         const Tile tl = tiles[mt];
         const int rows = tl.row1 - tl.row0;
         const int n0 = nt * BNm;
+        if constexpr (!PART && BM == 256) {
+            if (rows <= ThinShape<NMAT>::ROWS) {      // a thin tile: its own loop
+                if (tl.cnt == 1)
+                    pp_thin_item<NMAT, ACT, GATHER, kWStream>(lds, A, a_rows, gather_rows, B0, B1, C, tl.e, tl.row0,
+                                                              rows, n0, K, N);
+                else
+                    pp_thin_item<NMAT, ACT, GATHER, 0>(lds, A, a_rows, gather_rows, B0, B1, C, tl.e, tl.row0, rows,
+                                                       n0, K, N);
+                return;
+            }
+        }
         // the tile's rows split evenly over the four row quarters, at a multiple of 16 (an
         // expert with 256 rows in a 320-row tile multiplies 4 row blocks per wavefront,
         // not 5, 5, 5 and 1)
@@ -1686,7 +1903,7 @@ static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_
     static bool ready = false;
     static int occ = 1;
     unsigned G = 0;
-    constexpr size_t pp_bytes = PpShape<BM, NMAT>::LDS_BYTES;
+    constexpr size_t pp_bytes = pp_lds_bytes<BM, NMAT>();
     auto kpp = k_grouped_gemm_pp<BM, NMAT, ACT, GATHER, SPLIT>;
     hipError_t e = persistent_grid(kpp, pp_bytes, ready, occ, max_items, G, 512);
     if (e != hipSuccess) return e;

@@ -168,6 +168,47 @@ def test_grouped_ffn(lib, T, H, E, k, F, ffn, dtype):
     assert err <= tol_for(cfg)
 
 
+# Skewed per-expert counts on 256-row tiles (mean above 160 rows): tiles of at most 64 rows
+# (single-tile experts, and the ragged last tile of a long expert) take the ping-pong
+# kernel's thin-tile loop, the others its full K loop; empty experts, 1-row experts and the
+# 64 / 65-row boundary included; ragged K and N.  Then the same at K = 4096 (ordered
+# per-XCD fetch) and with a split-capable second projection (K = 4608).
+THIN_CASES = [  # counts per expert, H, F, ffn
+    ([1200, 1, 16, 17, 64, 65, 0, 300, 33, 5, 256, 63, 2000, 700, 40, 8], 264, 392, "swiglu"),
+    ([1200, 1, 16, 17, 64, 65, 0, 300, 33, 5, 256, 63, 2000, 700, 40, 8], 200, 520, "silu2"),
+    ([900, 3, 64, 1, 0, 48, 600, 17], 4096, 512, "swiglu"),
+    ([700, 20, 1, 64, 500, 2, 33, 9], 256, 4608, "silu2"),
+]
+
+
+@pytest.mark.parametrize("counts,H,F,ffn", THIN_CASES)
+def test_grouped_ffn_thin_tiles(lib, counts, H, F, ffn):
+    E, k = len(counts), 2
+    R = sum(counts)
+    T = (R + k - 1) // k
+    assert T * k / E > 160                     # 256-row tiles
+    cfg = MoEConfig("thin", T=T, H=H, E=E, k=k, F=F, ffn=ffn, dtype="bf16", bias="none", seed=5)
+    say(f"grouped_ffn thin tiles: counts {counts} H={H} F={F} {ffn}")
+    d = generate(cfg)
+    g = torch.Generator().manual_seed(R + H + F)
+    x_perm = torch.randn(T * k, H, generator=g).to(torch.bfloat16)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    y = lib.grouped_ffn(x_perm.cuda(), torch.from_numpy(offsets).cuda(), d["w_in"].cuda(),
+                        None if d["w_up"] is None else d["w_up"].cuda(), d["w_out"].cuda(), k, T)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(to_numpy(x_perm[:R]), offsets, weights_numpy(d), ffn)
+    got = to_numpy(y[:R])
+    err = normwise(got, ref)
+    # every expert's rows on their own, so a wrong thin tile cannot hide behind the big ones
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            assert normwise(got[a:b], ref[a:b]) <= tol_for(cfg), f"expert {e} ({b - a} rows)"
+    say(f"  normwise error {err:.3e}")
+    assert err <= tol_for(cfg)
+
+
 # ---------------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("T,k,H,dtype", [(1, 1, 8, torch.float32), (333, 2, 4096, torch.bfloat16),
