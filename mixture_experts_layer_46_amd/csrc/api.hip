@@ -40,7 +40,7 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout shared by every entry point (offsets from the workspace base).
 struct Layout {
-    size_t logits, topk_idx, topk_w, counts, offsets, segcnt, sorted_token, row_of_pair,
+    size_t logits, planes, topk_idx, topk_w, counts, offsets, segcnt, sorted_token, row_of_pair,
         tiles, ntiles, part_cnt, parts, h, y, total;
 };
 
@@ -65,6 +65,7 @@ Layout layout_of(const moe_shape& s) {
     Layout L{};
     size_t o = 0;
     L.logits = o;       o += up((size_t)gate_splits(s.T, s.H, s.E, s.dtype) * s.T * s.E * 4);
+    L.planes = o;       o += gate_uses_planes(s.T, s.dtype) ? up((size_t)3 * s.E * s.H * 2) : 0;
     L.topk_idx = o;     o += up(P * 4);
     L.topk_w = o;       o += up(P * 4);
     L.counts = o;       o += up((size_t)s.E * 4);
@@ -262,7 +263,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
     REQ(topk_w, "topk_w");
     if (s.T == 0) return MOE_OK;
     (void)hipGetLastError();
-    if (x) HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, 1, stream), "gate_logits");
+    if (x) HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, 1, nullptr, stream), "gate_logits");
     HIPCHK(launch_topk(logits, 1, nullptr, bias, topk_idx, topk_w, s.T, s.E, s.k, s.flags, stream), "topk");
     return MOE_OK;
 }
@@ -352,7 +353,8 @@ moe_status moe_forward_timed(const moe_shape* shape, const void* x, const float*
     int32_t* row_of_pair = at<int32_t>(workspace, L.row_of_pair);
     const int splits = gate_splits(s.T, s.H, s.E, s.dtype);
     if (events) HIPCHK(hipEventRecord(events[0], stream), "stage event");
-    HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, stream), "gate_logits");
+    bf16_t* planes = gate_uses_planes(s.T, s.dtype) ? at<bf16_t>(workspace, L.planes) : nullptr;
+    HIPCHK(launch_gate_logits(x, s.dtype, w_gate, logits, s.T, s.H, s.E, splits, planes, stream), "gate_logits");
     HIPCHK(launch_topk(logits, splits, nullptr, bias, idx, gw, s.T, s.E, s.k, s.flags, stream), "topk");
     if (events) HIPCHK(hipEventRecord(events[1], stream), "stage event");
     HIPCHK(launch_group(idx, P, s.k, s.E, s.capacity, at<int32_t>(workspace, L.segcnt),

@@ -45,8 +45,12 @@ void gemm_cfg_heights(GemmCfg c, int* bma, int* bmb);
 
 // K splits of the gate projection (partial sums [splits][T][E]) for a layer shape
 int gate_splits(long long T, int H, int E, int dtype);   // split-K ranges of the gate projection
+// whether the bf16 gate splits W_g into bf16 planes once per call (planes: 3 * E * H bf16
+// of workspace); `planes` NULL keeps the split inside each workgroup (moe_route, which has
+// no workspace)
+bool gate_uses_planes(long long T, int dtype);
 hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out,
-                              long long T, int H, int E, int splits, hipStream_t st);
+                              long long T, int H, int E, int splits, bf16_t* planes, hipStream_t st);
 // top-k over the sum of `nparts` partial logits; the sum goes to logits_out if not NULL
 hipError_t launch_topk(const float* logits, int nparts, float* logits_out, const float* bias,
                        int32_t* idx, float* w, long long T, int E, int k, unsigned flags,

@@ -281,6 +281,137 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_x3(const bf16_t* __restr
     }
 }
 
+// W_g [H, E] fp32 -> three bf16 planes [3][E][H] (expert-major, k contiguous) with
+// w = p0 + p1 + p2 exactly (split3_bf16), once per call, so that the gate projection's
+// workgroups copy 16-byte runs of k instead of splitting and transposing weights each.
+// Tile: 64 k x 64 experts through LDS (loads coalesced along E, stores along k).
+__global__ __launch_bounds__(256) void k_gate_split_planes(const float* __restrict__ wg, bf16_t* __restrict__ planes,
+                                                           int H, int E) {
+    __shared__ float tile[64][65];
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64, tid = threadIdx.x;
+    for (int i = tid; i < 64 * 64; i += 256) {
+        const int r = i >> 6, c = i & 63;
+        const int k = k0 + r, e = e0 + c;
+        tile[r][c] = (k < H && e < E) ? wg[(size_t)k * E + e] : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < 64 * 8; i += 256) {
+        const int c = i >> 3, kq = i & 7;          // expert e0 + c, k run k0 + 8 kq .. + 7
+        const int e = e0 + c, k = k0 + 8 * kq;
+        if (e >= E || k >= H) continue;            // H % 8 == 0: a run is all inside or all outside
+        float h[8], m[8], l[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split3_bf16(tile[8 * kq + j][c], h[j], m[j], l[j]);
+        const uint4 vh = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                                    pack_bf16x2(h[6], h[7]));
+        const uint4 vm = make_uint4(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m[4], m[5]),
+                                    pack_bf16x2(m[6], m[7]));
+        const uint4 vl = make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
+                                    pack_bf16x2(l[6], l[7]));
+        *reinterpret_cast<uint4*>(planes + ((size_t)0 * E + e) * H + k) = vh;
+        *reinterpret_cast<uint4*>(planes + ((size_t)1 * E + e) * H + k) = vm;
+        *reinterpret_cast<uint4*>(planes + ((size_t)2 * E + e) * H + k) = vl;
+    }
+}
+
+// The gate projection of k_gate_logits_x3 (same tile, wavefront grid and MFMA order) from
+// the pre-split planes: each 64-K step copies x and the three planes' 64-k runs into LDS
+// as 16-byte chunks (8 lanes per 128-byte row), with no conversion work in the loop.
+template <int TE>
+__global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ planes,
+                                                           float* __restrict__ out, int T, int H, int E,
+                                                           int kchunk) {
+    constexpr int TM = 256;
+    constexpr int NB = TE / 32;                 // 16-expert column blocks per wavefront
+    constexpr int FM = 4;                       // 16-token row blocks per wavefront
+    constexpr int WCH = 3 * TE * 8 / 512;       // plane chunks per thread per step
+    __shared__ __attribute__((aligned(16))) bf16_t sX[TM][GX_PITCH];
+    __shared__ __attribute__((aligned(16))) bf16_t sW[3][TE][GX_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
+    const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
+    const int xr0 = tid >> 3, xc = tid & 7;     // x: row (t >> 3) + 64 i, chunk t & 7
+    uint4 xr[4], wr[WCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = m0 + xr0 + 64 * i, kk = k0 + 8 * xc;
+            xr[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (t < T && kk < kend) xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {        // chunk (plane p, expert row r, k chunk c)
+            const int idx = tid + 512 * i, pr = idx >> 3, c = idx & 7;
+            const int pl = pr / TE, r = pr % TE;
+            const int e = e0 + r, kk = k0 + 8 * c;
+            wr[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (e < E && kk < kend) wr[i] = *reinterpret_cast<const uint4*>(planes + ((size_t)pl * E + e) * H + kk);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sX[xr0 + 64 * i][8 * xc]) = xr[i];
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int idx = tid + 512 * i, pr = idx >> 3, c = idx & 7;
+            *reinterpret_cast<uint4*>(&sW[pr / TE][pr % TE][8 * c]) = wr[i];
+        }
+    };
+    f32x4_t acc[FM][NB];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int fr = lane & 15, fq = lane >> 4;
+    if (kbeg < kend) {
+        gload(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (k0 + GT_K < kend) gload(k0 + GT_K);
+#pragma unroll
+            for (int ks = 0; ks < GT_K; ks += 32) {
+                bf16x8_t b[NB][3], a[FM];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        b[nb][p] = *reinterpret_cast<const bf16x8_t*>(
+                            &sW[p][wn * (TE / 2) + 16 * nb + fr][ks + 8 * fq]);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    a[fm] = *reinterpret_cast<const bf16x8_t*>(&sX[64 * wm + 16 * fm + fr][ks + 8 * fq]);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        // the small parts first
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
+                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
+                    }
+            }
+        }
+    }
+    float* o = out + (size_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int e = e0 + wn * (TE / 2) + 16 * nb + fr;
+        if (e >= E) continue;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = m0 + 64 * wm + fm * 16 + 4 * fq + v;
+                if (t < T) o[(size_t)t * E + e] = acc[fm][nb][v];
+            }
+    }
+}
+
 // ------------------------------------------------------------------------- top-k
 struct Cand {
     float s;    // ranking score (l + b)
@@ -424,8 +555,10 @@ int gate_splits(long long T, int H, int E, int dtype) {
     return (int)(sp < 1 ? 1 : sp);
 }
 
+bool gate_uses_planes(long long T, int dtype) { return T > 256 && dtype != MOE_F32; }
+
 hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out, long long T, int H,
-                              int E, int splits, hipStream_t st) {
+                              int E, int splits, bf16_t* planes, hipStream_t st) {
     const dim3 blk(256);
     const int kchunk = ((H + splits - 1) / splits + GT_K - 1) / GT_K * GT_K;
     const unsigned gy = (unsigned)((E + GT_E - 1) / GT_E);
@@ -442,6 +575,17 @@ hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* 
         const int te = gate_tile_experts(T, E, dtype);
         const dim3 grid((unsigned)((T + 255) / 256), (unsigned)((E + te - 1) / te), (unsigned)splits);
         const dim3 blk2(512);
+        if (planes) {
+            hipLaunchKernelGGL(k_gate_split_planes, dim3((unsigned)((H + 63) / 64), (unsigned)((E + 63) / 64)),
+                               dim3(256), 0, st, wg, planes, H, E);
+            if (te == 128)
+                hipLaunchKernelGGL((k_gate_logits_p3<128>), grid, blk2, 0, st, (const bf16_t*)x, planes, out, (int)T, H, E,
+                                   kchunk);
+            else
+                hipLaunchKernelGGL((k_gate_logits_p3<64>), grid, blk2, 0, st, (const bf16_t*)x, planes, out, (int)T, H, E,
+                                   kchunk);
+            return hipGetLastError();
+        }
         if (te == 128)
             hipLaunchKernelGGL((k_gate_logits_x3<128>), grid, blk2, 0, st, (const bf16_t*)x, wg, out, (int)T, H, E, kchunk);
         else
