@@ -244,6 +244,13 @@ E2E = [
     MoEConfig("one_token", T=1, H=64, E=8, k=2, F=64, ffn="swiglu", dtype="bf16", bias="none"),
     # 320-row tiles with skewed counts: hot experts span several tiles, cold ones a few rows
     MoEConfig("tiles_320_skew", T=1200, H=520, E=16, k=3, F=392, ffn="silu2", dtype="bf16", bias="zipf1.1"),
+    # bf16 above 256 tokens: the gate's per-call weight planes with a ragged expert count (37,
+    # a partial 64-expert tile and a partial 4-expert group) and H not a multiple of 64
+    MoEConfig("planes_ragged_E", T=700, H=136, E=37, k=3, F=200, ffn="swiglu", dtype="bf16", bias="normal0.5"),
+    # 128-expert gate tiles (E > 64) with a ragged last tile, zipf-skewed 256-row GEMM tiles
+    MoEConfig("planes_E200", T=2600, H=264, E=200, k=8, F=136, ffn="swiglu", dtype="bf16", bias="zipf1.1"),
+    # a single expert (E = k = 1) above 256 tokens: dense FFN through the bf16 path
+    MoEConfig("one_expert_bf16", T=300, H=256, E=1, k=1, F=512, ffn="silu2", dtype="bf16", bias="none"),
 ]
 
 
@@ -321,6 +328,8 @@ CAP_CASES = [  # capacity factor, layer (mean rows per expert picks the row tile
     (1.0, MoEConfig("cap", T=300, H=128, E=8, k=2, F=192, ffn="swiglu", dtype="bf16", bias="normal0.5")),
     # 300 rows per expert on average: the 256- and 320-row tile kernels, capped experts full
     (1.0, MoEConfig("cap_big", T=1200, H=264, E=8, k=2, F=392, ffn="silu2", dtype="bf16", bias="normal0.5")),
+    # skewed counts on 256-row tiles, capped: thin tiles beside capped full ones
+    (1.25, MoEConfig("cap_skew", T=2048, H=264, E=16, k=2, F=392, ffn="swiglu", dtype="bf16", bias="zipf1.1")),
 ]
 
 
