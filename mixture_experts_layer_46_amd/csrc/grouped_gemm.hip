@@ -1446,11 +1446,11 @@ __device__ __attribute__((always_inline)) inline void thin_step(
 
 // The whole thin tile: plan, prologue, K loop, epilogue.  Every value that selects memory
 // (the tile, the operand resources) is wavefront-uniform and kept in scalar registers.
-template <int NMAT, int ACT, bool GATHER, int WAUX>
+template <int NMAT, int ACT, bool GATHER, int WAUX, typename Claim>
 __device__ __attribute__((always_inline)) inline void pp_thin_item(
     lds_char* lds, const bf16_t* __restrict__ A, long long a_rows, const int32_t* __restrict__ gather_rows,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int e, int row0, int rows,
-    int n0, int K, int N) {
+    int n0, int K, int N, Claim&& claim) {
     using S = ThinShape<NMAT>;
     using P = PpShape<256, NMAT>;
     constexpr int BK = S::BK, BROW = P::BROW, BNm = P::BNm, CS_STRIDE = P::CS_STRIDE, NS = S::NS, LEAD = S::LEAD;
@@ -1536,6 +1536,7 @@ __device__ __attribute__((always_inline)) inline void pp_thin_item(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the zero loads past K land before LDS is reused
     __syncthreads();
+    claim();                                            // the next work item, during the epilogue
     // epilogue: activation, one rounding to bf16, staged in LDS, written as 16-byte row pieces
     typedef __attribute__((address_space(3))) bf16_t lds_bf16;
     lds_bf16* sC = reinterpret_cast<lds_bf16*>(lds);
@@ -1616,6 +1617,15 @@ __device__ __forceinline__ void gemm_tiles_pp(
     static_assert(!(SPLIT && GATHER), "only the second projection splits");
     float* const pbuf = SPLIT ? part_buf : nullptr;
 
+    // Work queues (item_q; the work order below).  Thread 0 claims the next work item from
+    // its XCD's queue once the current item's K loop is done (cn), so the atomic's latency
+    // passes during the epilogue.
+    const int xcd = blockIdx.x & 7, per_xcd = G >> 3;
+    int cn = 0;
+    auto claim = [&]() __attribute__((always_inline)) {
+        if (item_q && tid == 0) cn = atomicAdd(item_q + xcd, 1);
+    };
+
     // One work item: the whole K range (PART false), or part `part` of `nsplit` of the item
     // whose parts use slot `slot` of the part buffer.  The full rounds and the split tail run
     // in loops of their own, so the full rounds carry none of the split's state in registers.
@@ -1633,10 +1643,10 @@ __device__ __forceinline__ void gemm_tiles_pp(
             if (rows <= ThinShape<NMAT>::ROWS) {      // a thin tile: its own loop
                 if (tl.cnt == 1)
                     pp_thin_item<NMAT, ACT, GATHER, kWStream>(lds, A, a_rows, gather_rows, B0, B1, C, tl.e, tl.row0,
-                                                              rows, n0, K, N);
+                                                              rows, n0, K, N, claim);
                 else
                     pp_thin_item<NMAT, ACT, GATHER, 0>(lds, A, a_rows, gather_rows, B0, B1, C, tl.e, tl.row0, rows,
-                                                       n0, K, N);
+                                                       n0, K, N, claim);
                 return;
             }
         }
@@ -1683,6 +1693,7 @@ __device__ __forceinline__ void gemm_tiles_pp(
 #undef MOE_PP_ITEM
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the tail's zero loads land before LDS is reused
         __syncthreads();
+        claim();                                            // the next work item, during the epilogue
 
         // a split item: store this part; only the last part to arrive goes on, adding the
         // parts in part order (the item's slots are consecutive in the part buffer)
@@ -1717,32 +1728,83 @@ __device__ __forceinline__ void gemm_tiles_pp(
         main_end = wsp.split == 1 ? total : wsp.full;
     }
     // Work order.  The static order gives workgroup b the work indices first, first + G, ...
-    // (XCD b % 8 runs a contiguous chunk of G / 8 indices per round).  With item_q, the
-    // workgroups of an XCD instead take that XCD's indices in order from a counter, so the
-    // items running together on an XCD stay a contiguous window of the order (the row
-    // tiles and weight slices they share stay shared) even when items differ in length.
-    const int xcd = blockIdx.x & 7, per_xcd = G >> 3;
-    int* const q = item_q ? item_q + xcd : nullptr;
+    // (XCD b % 8 runs a contiguous chunk of G / 8 indices per round).  With item_q, XCD x's
+    // workgroups instead take the indices the static order gives XCD x in order from a
+    // counter (queue x), so the items running together on an XCD stay a contiguous window
+    // of the order (the row tiles and weight slices they share stay shared) even when
+    // items differ in length.  A workgroup whose queue is empty takes items from the next
+    // XCD's queue, and so on round the eight, so no XCD idles while another has items
+    // left (the queues' lengths differ with the launch's last round, and their items'
+    // costs with the experts' tiles).  The claim for the next item is made during the
+    // current one's epilogue; it reaches the other wavefronts through an LDS word, read
+    // between two barriers (the word lies in the rings the next item's DMA fills).
     int* const fetch_word = flag + 1;
-    auto fetch = [&]() -> long long {
-        if (tid == 0) *fetch_word = atomicAdd(q, 1);
-        __syncthreads();
-        const int c = *fetch_word;
-        __syncthreads();
-        return (long long)(c / per_xcd) * G + (long long)xcd * per_xcd + c % per_xcd;
+    // the work count: the items, or with the split the full rounds' items and the parts
+    auto work_count = [&]() -> long long {
+        const long long n = (long long)(*ntiles_p) * NT;
+        return SPLIT ? WorkSplit(n, G, pbuf ? KT : 0).nwork : n;
     };
-    long long w = q ? fetch() : first;
-    for (; w < main_end; w = q ? fetch() : w + G) run_item(w, 0, 1, -1, std::false_type{});
-    if constexpr (SPLIT) {
-        // the split is derived again from the tile count (reloaded after the loop's memory
-        // clobbers), so that none of it is held through the full rounds
-        const WorkSplit wsp((long long)(*ntiles_p) * NT, G, pbuf ? KT : 0);
-        for (; w < wsp.nwork; w = q ? fetch() : w + G) {
-            long long item;
-            int part, slot;
-            wsp.item_of(w, item, part, slot);
-            run_item(item, __builtin_amdgcn_readfirstlane(part), wsp.split, __builtin_amdgcn_readfirstlane(slot),
-                     std::true_type{});
+    // thread 0: the work index of claim c on this XCD's queue; past its end, an item of the
+    // first other queue (in XCD order from this one) that still holds one, or -1.  A queue
+    // once empty stays empty, so one pass that finds each queue empty (by its count or by
+    // a claim past its end) proves all are.
+    auto resolve = [&](int c) -> int {
+        const long long nw = work_count();
+        const long long rounds = nw / G, rem = nw - rounds * G;
+        auto qlen = [&](int v) {
+            return rounds * per_xcd + min(max(rem - (long long)v * per_xcd, 0LL), (long long)per_xcd);
+        };
+        auto index = [&](int v, long long i) { return (int)((i / per_xcd) * G + (long long)v * per_xcd + i % per_xcd); };
+        if (c < qlen(xcd)) return index(xcd, c);
+        int seen[8];
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            seen[i] = __hip_atomic_load(item_q + ((xcd + i) & 7), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 1; i < 8; ++i) {
+            const int v = (xcd + i) & 7;
+            const long long len = qlen(v);
+            if (seen[i] >= len) continue;
+            const int cv = atomicAdd(item_q + v, 1);
+            if (cv < len) return index(v, cv);
+        }
+        return -1;
+    };
+    auto next = [&](long long cur) -> long long {
+        if (!item_q) {
+            const long long n = cur + G;
+            return n < work_count() ? n : -1;
+        }
+        if (tid == 0) *fetch_word = resolve(cn);
+        __syncthreads();
+        const int v = *fetch_word;
+        __syncthreads();
+        return v;
+    };
+    long long w;
+    if (item_q) {
+        if (tid == 0) *fetch_word = resolve(atomicAdd(item_q + xcd, 1));
+        __syncthreads();
+        w = *fetch_word;
+        __syncthreads();
+    } else {
+        w = first < work_count() ? first : -1;
+    }
+    // full items (every item when the launch does not split), then split parts; a queue
+    // taken over from another XCD may hand out a full item after a part
+    while (w >= 0) {
+        for (; w >= 0 && w < main_end; w = next(w)) run_item(w, 0, 1, -1, std::false_type{});
+        if constexpr (!SPLIT) break;                 // every index is below main_end
+        else {
+            // the split is derived again from the tile count (reloaded after the loop's
+            // memory clobbers), so that none of it is held through the full items
+            const WorkSplit wsp((long long)(*ntiles_p) * NT, G, pbuf ? KT : 0);
+            for (; w >= main_end; w = next(w)) {
+                long long item;
+                int part, slot;
+                wsp.item_of(w, item, part, slot);
+                run_item(item, __builtin_amdgcn_readfirstlane(part), wsp.split,
+                         __builtin_amdgcn_readfirstlane(slot), std::true_type{});
+            }
         }
     }
 }
@@ -1892,12 +1954,6 @@ static hipError_t persistent_grid(KernT kern, size_t lds_bytes, bool& ready, int
 // projection and was 3% slower on the second, so the 4-wavefront kernel stays.
 constexpr bool kPp320 = false;
 
-// The ordered per-XCD fetch costs an atomic and two barriers per item, which items of
-// under 128 K steps (4096 of K) do not earn back: they keep the static order.  On the
-// fine-grained skewed shape the fetch took the first projection (224 steps) from 4.58
-// to 4.38 ms, and made the second (64 steps) 1.3% slower.
-constexpr int kFetchMinSteps = 128;
-
 // One ping-pong kernel of a launch pair (BM-row tiles), split-capable or not.
 template <int BM, int NMAT, int ACT, bool GATHER, bool SPLIT>
 static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_rows, const void* B0,
@@ -1912,7 +1968,7 @@ static hipError_t run_pp(const void* A, long long a_rows, const int32_t* gather_
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kpp, dim3(G), dim3(512), pp_bytes, st, (const bf16_t*)A, gather_rows, (const bf16_t*)B0,
                        (const bf16_t*)B1, (bf16_t*)C, tiles, ntiles, K, N, a_rows, sb.parts, sb.counts,
-                       (G % 8 == 0 && (K + 31) / 32 >= kFetchMinSteps) ? sb.queue : nullptr);
+                       G % 8 == 0 ? sb.queue : nullptr);
     return hipGetLastError();
 }
 
