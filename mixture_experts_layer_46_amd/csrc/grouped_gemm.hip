@@ -682,6 +682,10 @@ __device__ __attribute__((always_inline)) inline void kloop_early(
 // otherwise leads the compiler to drain every DMA in flight (vmcnt(0)) at each step; the
 // memory clobber still keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void kloop_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt lgkmcnt(0) as the builtin (gfx9 encoding: vmcnt and expcnt at their maxima), so
+// that the compiler knows the fragment reads have landed: after the same wait written as
+// inline asm it put a redundant lgkmcnt wait before each MFMA of the next phase.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Split of the last round's items along K.  A persistent launch of G workgroups runs its
 // items in rounds of G; when the last round is partial, its items are split along K into
@@ -1251,13 +1255,14 @@ __device__ __attribute__((always_inline)) inline void pp_kloop(
                           g, wn, af, bfr);
         __builtin_amdgcn_sched_barrier(0);
         pp_dma_step<BM, NMAT, GROUP, WAUX>(lds, ra, rb0, rb1, pl, kt0, kt, K, rowB, wave);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_lgkm0();
         if constexpr (GROUP == 1) wait_vmcnt<VMCNT>();           // step kt + 1 complete
         kloop_barrier();
-        // MFMA phase
+        // MFMA phase (the guards are laid out as fall-throughs: a full tile takes no branch;
+        // with the compiler's own layout it took two or three per step)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            if (fm < nblk) {
+            if (__builtin_expect(fm < nblk, 1)) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
@@ -1526,7 +1531,7 @@ __device__ __attribute__((always_inline)) inline void pp_thin_item(
         // and its fragment reads of step s - 1 are done; after the barrier both hold for all
         if (wave < S::AINSTR) wait_vmcnt<(LEAD - 1) * 3>();
         else wait_vmcnt<(LEAD - 1) * 2>();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_lgkm0();
         kloop_barrier();
         const int cur = s % NS, nxt = (s + LEAD) % NS;       // nxt: the stage step s - 1 used
         thin_step<NMAT, WAUX>(lds + S::A_RING + cur * S::A_STAGE, lds + S::W_RING + cur * S::B_STAGE,
