@@ -1057,6 +1057,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_lds(
 // ------------------------------------------- ping-pong variant (two wavefront groups)
 // Same tiles, LDS layout and DMA as above, with 8 wavefronts per workgroup in two groups
 // of four (one wavefront of each group per SIMD, at most 128 accumulator registers each).
+// Each group owns half the tile's rows; its four wavefronts split the columns.
 // Each K step has a read phase (DMA issue and fragment reads) and an MFMA phase; the
 // groups run them out of step, so one group's LDS reads and DMA issue overlap the other
 // group's MFMAs.  Between two consecutive barriers one group is in its read phase and the
@@ -1080,7 +1081,13 @@ struct PpShape {
     // ring depths: 320-row tiles stream their weights from HBM, 7 steps ahead
     static constexpr int NA = BM == 320 ? 3 : 4, NW = BM == 320 ? 8 : 4;
     static constexpr int GM = BM / 2;                        // rows of one group
-    static constexpr int WTM = GM / 2, WTN = BN / 2;         // wavefront tile (2 x 2 per group)
+    // A group's four wavefronts split its 128 x 256 tile by columns, 128 x 64 each: every
+    // wavefront reads all the group's A rows (ds_read_b128) and a quarter of the W columns
+    // (ds_read_b64_tr_b16, about half the rate per byte), so a K step costs the LDS some
+    // 17% fewer clocks than with 64 x 128 tiles (2 x 2), at the same 128 accumulators.
+    // 320-row tiles keep 2 x 2 (160 x 96).
+    static constexpr int WCOLS = BM == 320 ? 2 : 4, WROWS = 4 / WCOLS;
+    static constexpr int WTM = GM / WROWS, WTN = BN / WCOLS; // wavefront tile
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static constexpr int A_STAGE = BM * BK * 2, B_STAGE = BK * LBN * 2;
     static constexpr int W_RING = NA * A_STAGE;              // LDS offset of the W ring
@@ -1324,7 +1331,7 @@ __device__ __forceinline__ void pp_write_out(lds_char* lds, BlockFn block, int n
         if (fm >= nblk) break;                 // blocks past the wavefront's rows
 #pragma unroll
         for (int fo = 0; fo < FO; ++fo) {
-            const int col = (NMAT == 2 ? wn * (BNm / 2) : wn * WTN) + 16 * fo + l16;
+            const int col = wn * (WTN / NMAT) + 16 * fo + l16;
             const f32x4_t x = block(fm, fo);
             f32x4_t u = x;
             if constexpr (NMAT == 2) u = block(fm, fo + FN / 2);
@@ -1600,8 +1607,8 @@ __device__ __forceinline__ void gemm_tiles_pp(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wsub = (wave >> 1) & 1, wn = wave & 1;
-    const int wr = 2 * grp + wsub;                               // this wavefront's row quarter
+    const int grp = wave >> 2, wsub = (wave & 3) / S::WCOLS, wn = wave % S::WCOLS;
+    const int wr = S::WROWS * grp + wsub;                        // this wavefront's row piece
     const int l16 = lane & 15, lq = lane >> 4;
 
     const int NT = (N + BNm - 1) / BNm;
@@ -1655,10 +1662,11 @@ __device__ __forceinline__ void gemm_tiles_pp(
                 return;
             }
         }
-        // the tile's rows split evenly over the four row quarters, at a multiple of 16 (an
-        // expert with 256 rows in a 320-row tile multiplies 4 row blocks per wavefront,
-        // not 5, 5, 5 and 1)
-        const int rsplit = min(WTM, (rows + 63) / 64 * 16);
+        // the tile's rows split evenly over the row pieces (one per group; two per group for
+        // 320-row tiles), at a multiple of 16 (an expert with 256 rows in a 320-row tile
+        // multiplies 4 row blocks per wavefront, not 5, 5, 5 and 1)
+        constexpr int NPIECE = 2 * S::WROWS;
+        const int rsplit = min(WTM, (rows + 16 * NPIECE - 1) / (16 * NPIECE) * 16);
         const int row0 = wr * rsplit;                            // first tile row of this wavefront
         const int wrows = min(rows - row0, rsplit);
         const int nblk = wrows > 0 ? (wrows + 15) / 16 : 0;
