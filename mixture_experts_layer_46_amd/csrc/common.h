@@ -42,4 +42,26 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// ------------------------------------------------ direct-to-LDS operand loads (DMA)
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr uint32_t kOOB = 0x80000000u;          // an offset past every buffer: reads zeros
+
+// A raw buffer resource over [base, base + bytes): loads past the end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Swizzle of LDS rows of 64 bytes (four 16-byte chunks, one K step of 32 bf16): chunk q of
+// row m sits at slot q ^ swa4(m).  On gfx950 a ds_read_b128 serves 16 lanes per LDS cycle
+// (64 banks), grouped by bit2^bit3^bit4 of the lane index (lanes 0-3, 12-15 and 20-27
+// share a cycle; measured with the bank-conflict counter); an MFMA fragment read has lane
+// l on row l & 15, chunk l >> 4.  With swa4(m) = (m >> 1) & 2 the 16 lanes of every cycle
+// land on distinct bank quads.
+__device__ __forceinline__ int swa4(int m) { return (m >> 1) & 2; }
+
 }  // namespace moe

@@ -294,8 +294,6 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 //     the 320 x 192 tile with wavefront tiles of 160 x 96.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Zeroes one accumulator as a value of its own: with a zero constant shared by several
 // accumulators, the register allocator may not update them in place in the K loop and
@@ -321,19 +319,8 @@ __device__ __forceinline__ int wblk(int blk, int g) {
     if constexpr (BM == 320) return NMAT == 1 ? ((blk & ~3) | ((blk & 3) ^ g)) : ((blk & ~1) | ((blk & 1) ^ g));
     else return (blk & ~7) | ((blk & 7) ^ g);
 }
-// A-row swizzle: 16-byte chunk q of tile row m sits at slot q ^ swa4(m).  On gfx950 a
-// ds_read_b128 serves 16 lanes per LDS cycle (64 banks), grouped by bit2^bit3^bit4 of
-// the lane index (lanes 0-3, 12-15 and 20-27 share a cycle; measured with the bank-
-// conflict counter); a fragment read has lane l on row l & 15, chunk l >> 4.  With
-// swa4(m) = (m >> 1) & 2 the 16 lanes of every cycle land on distinct bank quads.
-__device__ __forceinline__ int swa4(int m) { return (m >> 1) & 2; }
-
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kWStream = 2;                     // the nt bit of a buffer load's cache policy          // an offset past every buffer: reads zeros
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
+// A rows use the 64-byte row swizzle swa4 (common.h).
+constexpr int kWStream = 2;                     // the nt bit of a buffer load's cache policy
 
 // Tile shapes: BM x BN outputs (BN over both matrices for SwiGLU).  The 320-row tile is
 // 192 wide so that its accumulators (60 16x16 blocks per wavefront) still fit the AGPRs;
@@ -379,8 +366,6 @@ struct LdsShape {
     static_assert((NW - 1) * DPW < 64, "DMA in flight fits the 6-bit vmcnt");
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Per-tile DMA description (one wavefront's share of a K step).
 template <int ADMA, int BDMA>

@@ -314,88 +314,154 @@ __global__ __launch_bounds__(256) void k_gate_split_planes(const float* __restri
     }
 }
 
-// The gate projection of k_gate_logits_x3 (same tile, wavefront grid and MFMA order) from
-// the pre-split planes: each 64-K step copies x and the three planes' 64-k runs into LDS
-// as 16-byte chunks (8 lanes per 128-byte row), with no conversion work in the loop.
+// The gate projection from the pre-split planes, with its operands streamed into LDS by
+// direct-to-LDS buffer loads (no register staging: a register stage covered one 64-K step
+// of MFMAs against a load latency about twice as long).  Tile: 256 tokens x TE experts,
+// eight wavefronts in a 4 x 2 grid (64 tokens x TE/2 experts each, two per SIMD), K steps
+// of 32.  A stage holds x (256 rows of 64 bytes) and the three planes (3 TE rows of 64
+// bytes), rows swizzled with swa4 for the fragment reads; GS_NS stages, the DMA GS_LEAD
+// steps ahead, one barrier per step.  Every step issues the same DMA (steps past the K
+// range load zeros into a stage nobody reads), so each wavefront waits with a constant
+// count.  MFMA order per step and 16-expert block: the plane of the smallest parts first.
+constexpr int GS_NS = 4, GS_LEAD = GS_NS - 1;
+
+// keeps an accumulator in AGPRs (the MFMA then accumulates in place)
+__device__ __forceinline__ void gs_pin_acc(f32x4_t& a) { asm volatile("" : "+a"(a)); }
+// one 16-byte-per-lane direct-to-LDS load (1 KB per wavefront) at dst
+__device__ __forceinline__ void gs_dma(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+// this wavefront's fragment reads are done, then every wavefront's (a bare s_barrier: the
+// fence of __syncthreads would also wait for the DMA in flight)
+__device__ __forceinline__ void gs_step_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <int TE>
+struct GateStage {
+    static constexpr int TM = 256, BK = 32;
+    static constexpr int X_BYTES = TM * BK * 2;              // 16 KB
+    static constexpr int W_BYTES = 3 * TE * BK * 2;          // 24 KB (TE 128) or 12 KB
+    static constexpr int BYTES = X_BYTES + W_BYTES;
+    static constexpr int NI = BYTES / 1024;                  // 1 KB DMA instructions per stage
+    static constexpr int DPW_HI = (NI + 7) / 8, DPW_LO = NI / 8;   // per wavefront
+    static constexpr int LDS = GS_NS * BYTES;
+    static_assert(LDS <= 160 * 1024, "the stages fit the LDS");
+    static_assert(NI % 8 == 0 || DPW_HI == DPW_LO + 1, "two DMA counts at most");
+};
+
 template <int TE>
 __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ planes,
                                                            float* __restrict__ out, int T, int H, int E,
                                                            int kchunk) {
-    constexpr int TM = 256;
+    using S = GateStage<TE>;
+    constexpr int TM = S::TM, BK = S::BK, NI = S::NI;
     constexpr int NB = TE / 32;                 // 16-expert column blocks per wavefront
     constexpr int FM = 4;                       // 16-token row blocks per wavefront
-    constexpr int WCH = 3 * TE * 8 / 512;       // plane chunks per thread per step
-    __shared__ __attribute__((aligned(16))) bf16_t sX[TM][GX_PITCH];
-    __shared__ __attribute__((aligned(16))) bf16_t sW[3][TE][GX_PITCH];
+    constexpr int DMAX = S::DPW_HI;
+    extern __shared__ uint4 gsmem[];
+    lds_char* lds = (lds_char*)gsmem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
     const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
-    const int xr0 = tid >> 3, xc = tid & 7;     // x: row (t >> 3) + 64 i, chunk t & 7
-    uint4 xr[4], wr[WCH];
-    auto gload = [&](int k0) {
+    const int KT = kbeg < kend ? (kend - kbeg + BK - 1) / BK : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(planes, (uint32_t)((size_t)3 * E * H * 2));
+    // this wavefront's DMA instructions j = wave + 8 i (j < NI): x rows 16 j .. 16 j + 15
+    // for j < 16, else plane rows 16 (j - 16) ..; each lane moves one 16-byte chunk
+    uint32_t off[DMAX], kq[DMAX];
+    bool isx[DMAX];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = m0 + xr0 + 64 * i, kk = k0 + 8 * xc;
-            xr[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (t < T && kk < kend) xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + kk);
+    for (int i = 0; i < DMAX; ++i) {
+        const int j = wave + 8 * i;
+        isx[i] = j < 16;
+        off[i] = kOOB;
+        kq[i] = 0;
+        if (j < NI) {
+            const int r = (isx[i] ? j : j - 16) * 16 + (lane >> 2);   // row in the x or plane region
+            const int q = (lane & 3) ^ swa4(r);
+            kq[i] = (uint32_t)(kbeg + 8 * q);
+            if (isx[i]) {
+                const int t = m0 + r;
+                if (t < T) off[i] = (uint32_t)(((size_t)t * H + kbeg + 8 * q) * 2);
+            } else {
+                const int pl = r / TE, e = e0 + r % TE;
+                if (e < E) off[i] = (uint32_t)((((size_t)pl * E + e) * H + kbeg + 8 * q) * 2);
+            }
         }
+    }
+    auto dma = [&](int step) {                  // the DMA of K step `step` into its stage
+        lds_char* st = lds + (step % GS_NS) * S::BYTES;
 #pragma unroll
-        for (int i = 0; i < WCH; ++i) {        // chunk (plane p, expert row r, k chunk c)
-            const int idx = tid + 512 * i, pr = idx >> 3, c = idx & 7;
-            const int pl = pr / TE, r = pr % TE;
-            const int e = e0 + r, kk = k0 + 8 * c;
-            wr[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (e < E && kk < kend) wr[i] = *reinterpret_cast<const uint4*>(planes + ((size_t)pl * E + e) * H + kk);
+        for (int i = 0; i < DMAX; ++i) {
+            const int j = wave + 8 * i;
+            if (j < NI) {
+                const uint32_t dk = (uint32_t)step * BK;
+                const uint32_t o = (off[i] != kOOB && step < KT && kq[i] + dk < (uint32_t)kend) ? off[i] + dk * 2 : kOOB;
+                gs_dma(isx[i] ? rx : rp, st + j * 1024, o);
+            }
         }
     };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sX[xr0 + 64 * i][8 * xc]) = xr[i];
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) {
-            const int idx = tid + 512 * i, pr = idx >> 3, c = idx & 7;
-            *reinterpret_cast<uint4*>(&sW[pr / TE][pr % TE][8 * c]) = wr[i];
-        }
+    auto wait_step = [&]() {                    // this wavefront's DMA of the current step has landed
+        if (NI % 8 == 0 || wave < NI % 8) wait_vmcnt<S::DPW_HI * (GS_LEAD - 1)>();
+        else wait_vmcnt<S::DPW_LO * (GS_LEAD - 1)>();
     };
     f32x4_t acc[FM][NB];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int fr = lane & 15, fq = lane >> 4;
-    if (kbeg < kend) {
-        gload(kbeg);
-        for (int k0 = kbeg; k0 < kend; k0 += GT_K) {
-            __syncthreads();
-            lstore();
-            __syncthreads();
-            if (k0 + GT_K < kend) gload(k0 + GT_K);
-#pragma unroll
-            for (int ks = 0; ks < GT_K; ks += 32) {
-                bf16x8_t b[NB][3], a[FM];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int p = 0; p < 3; ++p)
-                        b[nb][p] = *reinterpret_cast<const bf16x8_t*>(
-                            &sW[p][wn * (TE / 2) + 16 * nb + fr][ks + 8 * fq]);
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    a[fm] = *reinterpret_cast<const bf16x8_t*>(&sX[64 * wm + 16 * fm + fr][ks + 8 * fq]);
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        // the small parts first
-                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
-                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
-                        acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
-                    }
-            }
+        for (int j = 0; j < NB; ++j) {
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            gs_pin_acc(acc[i][j]);
         }
+    const int fr = lane & 15, fq = lane >> 4;
+    // fragment read offsets within a stage
+    int a_rd[FM], b_rd[NB];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int r = 64 * wm + 16 * fm + fr;
+        a_rd[fm] = r * 64 + ((fq ^ swa4(r)) << 4);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = wn * (TE / 2) + 16 * nb + fr;
+        b_rd[nb] = S::X_BYTES + r * 64 + ((fq ^ swa4(r)) << 4);
+    }
+    if (KT > 0) {
+#pragma unroll
+        for (int st = 0; st < GS_LEAD; ++st) dma(st);
+        for (int s = 0; s < KT; ++s) {
+            wait_step();
+            gs_step_barrier();                                  // reads of step s - 1 done; step s landed
+            dma(s + GS_LEAD);                                   // into the stage step s - 1 used
+            const lds_char* cur = lds + (s % GS_NS) * S::BYTES;
+            bf16x8_t a[FM], b[NB][3];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) a[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(cur + a_rd[fm]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[nb][p] = *(const __attribute__((address_space(3))) bf16x8_t*)(cur + b_rd[nb] + p * TE * 64);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    // the small parts first
+                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
+                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
+                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
+                }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) gs_pin_acc(acc[fm][nb]);
+        }
+        wait_vmcnt<0>();                        // the zero loads past the K range land before exit
     }
     float* o = out + (size_t)blockIdx.z * T * E;
 #pragma unroll
@@ -579,11 +645,11 @@ hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* 
             hipLaunchKernelGGL(k_gate_split_planes, dim3((unsigned)((H + 63) / 64), (unsigned)((E + 63) / 64)),
                                dim3(256), 0, st, wg, planes, H, E);
             if (te == 128)
-                hipLaunchKernelGGL((k_gate_logits_p3<128>), grid, blk2, 0, st, (const bf16_t*)x, planes, out, (int)T, H, E,
-                                   kchunk);
+                hipLaunchKernelGGL((k_gate_logits_p3<128>), grid, blk2, GateStage<128>::LDS, st, (const bf16_t*)x,
+                                   planes, out, (int)T, H, E, kchunk);
             else
-                hipLaunchKernelGGL((k_gate_logits_p3<64>), grid, blk2, 0, st, (const bf16_t*)x, planes, out, (int)T, H, E,
-                                   kchunk);
+                hipLaunchKernelGGL((k_gate_logits_p3<64>), grid, blk2, GateStage<64>::LDS, st, (const bf16_t*)x,
+                                   planes, out, (int)T, H, E, kchunk);
             return hipGetLastError();
         }
         if (te == 128)
