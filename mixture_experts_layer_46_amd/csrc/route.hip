@@ -527,21 +527,35 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     if (t >= T) return;
     const bool select_only = flags & MOE_FLAG_BIAS_SELECT_ONLY;
     const bool no_renorm = flags & MOE_FLAG_NO_RENORM;
-    float s[4], g[4];
+    float s[4], g[4], l[4];
     bool live[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+        live[q] = lane + 64 * q < E;
+        l[q] = live[q] ? logits[t * E + lane + 64 * q] : 0.f;
+    }
+    // the later partial sums, added in part order; loaded four parts at a time so that
+    // the loads are in flight together
+    for (int p = 1; p < nparts; p += 4) {
+        float v[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[q][i] = (live[q] && p + i < nparts) ? logits[(long long)(p + i) * T * E + t * E + lane + 64 * q] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (p + i < nparts) l[q] += v[q][i];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        live[q] = e < E;
-        float l = 0.f;
-        if (live[q]) {
-            l = logits[t * E + e];
-            for (int p = 1; p < nparts; ++p) l += logits[(long long)p * T * E + t * E + e];
-            if (logits_out) logits_out[t * E + e] = l;
-        }
+        if (live[q] && logits_out) logits_out[t * E + e] = l[q];
         const float b = (live[q] && bias) ? bias[e] : 0.f;
-        s[q] = l + b;                       // one fp32 add: the ranking score
-        g[q] = select_only ? l : s[q];      // what the gate is computed from
+        s[q] = l[q] + b;                    // one fp32 add: the ranking score
+        g[q] = select_only ? l[q] : s[q];   // what the gate is computed from
     }
     int sel_i[8];
     float sel_g[8];
