@@ -6,8 +6,8 @@
 //
 // out[t] = sum_j g[t, j] * y_perm[row_of_pair[t*k + j]]  ([FourStage §2.4]: every token
 // sums its k expert outputs weighted by their gates; [Principles §2.2]).  One
-// workgroup per token gathers its k grouped rows (16-byte loads, all k issued before
-// any use), accumulates in fp32 in slot order and rounds once.  Each output row is
+// workgroup per token gathers its k grouped rows (16-byte loads, two chunks' worth issued
+// before any use), accumulates in fp32 in slot order and rounds once.  Each output row is
 // written by exactly one workgroup, so there are no atomics and no ordering races.
 // Each grouped row is read once, by its token's workgroup: the loads carry the
 // non-temporal hint (fine-grained skewed layer: 0.214 -> 0.195 ms).
@@ -16,6 +16,50 @@
 
 namespace moe {
 
+// One 16-byte chunk of an output row: the k grouped rows' chunks (already loaded), weighted
+// in slot order in fp32, rounded once.
+template <bool BF16>
+__device__ __forceinline__ uint4 combine_chunk(const uint4 (&v)[8], const int (&rows)[8], const float (&g)[8]) {
+    constexpr int NV = BF16 ? 8 : 4;
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (rows[j] < 0) continue;
+        const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        if constexpr (BF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += g[j] * bf16lo_to_f32(d[q]);
+                acc[2 * q + 1] += g[j] * bf16hi_to_f32(d[q]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += g[j] * __uint_as_float(d[q]);
+        }
+    }
+    uint4 o;
+    if constexpr (BF16) {
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+    } else {
+        o.x = __float_as_uint(acc[0]);
+        o.y = __float_as_uint(acc[1]);
+        o.z = __float_as_uint(acc[2]);
+        o.w = __float_as_uint(acc[3]);
+    }
+    return o;
+}
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
+// Each thread takes two chunks per pass (c and c + 256), so that 2k loads are in flight
+// before any use.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y,
                                                  const int32_t* __restrict__ row_of_pair,
@@ -29,45 +73,18 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y,
         rows[j] = (j < k) ? row_of_pair[t * k + j] : -1;
         g[j] = (j < k) ? w[t * k + j] : 0.f;
     }
-    for (int c = threadIdx.x; c < chunks; c += 256) {
-        uint4 v[8];
+    for (int c = threadIdx.x; c < chunks; c += 512) {
+        const bool two = c + 256 < chunks;
+        uint4 v0[8], v1[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (rows[j] >= 0)
-                v[j] = __builtin_bit_cast(
-                    uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y + (long long)rows[j] * chunks + c)));
-        constexpr int NV = BF16 ? 8 : 4;
-        float acc[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (rows[j] < 0) continue;
-            const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-            if constexpr (BF16) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] += g[j] * bf16lo_to_f32(d[q]);
-                    acc[2 * q + 1] += g[j] * bf16hi_to_f32(d[q]);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] += g[j] * __uint_as_float(d[q]);
+            if (rows[j] >= 0) {
+                const uint4* yr = y + (long long)rows[j] * chunks + c;
+                v0[j] = load_nt(yr);
+                if (two) v1[j] = load_nt(yr + 256);
             }
-        }
-        uint4 o;
-        if constexpr (BF16) {
-            o.x = pack_bf16x2(acc[0], acc[1]);
-            o.y = pack_bf16x2(acc[2], acc[3]);
-            o.z = pack_bf16x2(acc[4], acc[5]);
-            o.w = pack_bf16x2(acc[6], acc[7]);
-        } else {
-            o.x = __float_as_uint(acc[0]);
-            o.y = __float_as_uint(acc[1]);
-            o.z = __float_as_uint(acc[2]);
-            o.w = __float_as_uint(acc[3]);
-        }
-        out[t * chunks + c] = o;
+        out[t * chunks + c] = combine_chunk<BF16>(v0, rows, g);
+        if (two) out[t * chunks + c + 256] = combine_chunk<BF16>(v1, rows, g);
     }
 }
 
