@@ -1590,11 +1590,10 @@ __device__ __forceinline__ void gemm_tiles_pp(
     bf16_t* sC = reinterpret_cast<bf16_t*>(smem);
     int* flag = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + S::FLAG_OFF);
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wsub = (wave & 3) / S::WCOLS, wn = wave % S::WCOLS;
     const int wr = S::WROWS * grp + wsub;                        // this wavefront's row piece
-    const int l16 = lane & 15, lq = lane >> 4;
 
     const int NT = (N + BNm - 1) / BNm;
     const int KT = (K + BK - 1) / BK;
@@ -1602,14 +1601,6 @@ __device__ __forceinline__ void gemm_tiles_pp(
     const int G = gridDim.x;
     const long long first = (long long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t rowB = (uint32_t)N * 2;
-    // A fragment reads at row 0 of the wavefront's rows (the rows move per item, by
-    // multiples of 16, which keep the A swizzle)
-    const int a_rd0 = l16 * (BK * 2) + ((lq ^ swa4(l16)) << 4);
-    // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
-    const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
-    const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
-    // this wavefront's accumulators in a part slot (register layout, 16 bytes per lane per block)
-    const uint32_t wofs = (uint32_t)((wave * FM * FN * 256 + lane * 4) * 4);
 
     static_assert(!(SPLIT && GATHER), "only the second projection splits");
     float* const pbuf = SPLIT ? part_buf : nullptr;
@@ -1629,6 +1620,18 @@ __device__ __forceinline__ void gemm_tiles_pp(
     auto run_item = [&](long long item, int part, int nsplit, int slot, auto split_tag)
                         __attribute__((always_inline)) {
         constexpr bool PART = decltype(split_tag)::value;
+        // per-lane constants, derived here from an opaque copy of the thread index: kept
+        // live across the K loops they were spilled, and reloading them cost every item
+        // some 5k cycles of serialized scratch reads
+        int tid_o = threadIdx.x;
+        asm volatile("" : "+v"(tid_o));
+        const int lane = tid_o & 63, l16 = lane & 15, lq = lane >> 4;
+        // A fragment reads at row 0 of the wavefront's rows (the rows move per item, by
+        // multiples of 16, which keep the A swizzle)
+        const int a_rd0 = l16 * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+        // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
+        const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
+        const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
         int mt, nt;
         item_coords(item, NT, tiles, mt, nt);
         mt = __builtin_amdgcn_readfirstlane(mt);
@@ -1746,14 +1749,23 @@ __device__ __forceinline__ void gemm_tiles_pp(
     // first other queue (in XCD order from this one) that still holds one, or -1.  A queue
     // once empty stays empty, so one pass that finds each queue empty (by its count or by
     // a claim past its end) proves all are.
+    auto qlen_of = [&](int v) -> long long {
+        const long long nw = work_count();
+        const long long rounds = nw / G, rem = nw - rounds * G;
+        return rounds * per_xcd + min(max(rem - (long long)v * per_xcd, 0LL), (long long)per_xcd);
+    };
+    // this XCD's queue length, fixed for the launch: the common case of resolve below is a
+    // claim inside it, taken without reloading the tile count or 64-bit divisions (those had
+    // made the hand-off between two items some 5k cycles)
+    const int own_len = item_q ? __builtin_amdgcn_readfirstlane((int)qlen_of(xcd)) : 0;
     auto resolve = [&](int c) -> int {
+        if (c < own_len) return (c / per_xcd) * G + xcd * per_xcd + c % per_xcd;
         const long long nw = work_count();
         const long long rounds = nw / G, rem = nw - rounds * G;
         auto qlen = [&](int v) {
             return rounds * per_xcd + min(max(rem - (long long)v * per_xcd, 0LL), (long long)per_xcd);
         };
         auto index = [&](int v, long long i) { return (int)((i / per_xcd) * G + (long long)v * per_xcd + i % per_xcd); };
-        if (c < qlen(xcd)) return index(xcd, c);
         int seen[8];
 #pragma unroll
         for (int i = 1; i < 8; ++i)
