@@ -868,10 +868,9 @@ __device__ __forceinline__ void gemm_tiles(
     constexpr size_t SLOT = (size_t)BM * S::BN;       // floats per part slot
     static_assert(SLOT <= kGemmPartSlotFloats, "part slot larger than the workspace's");
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int l16 = lane & 15, lq = lane >> 4;
 
     const int NT = (N + BNm - 1) / BNm;
     const int KT = (K + BK - 1) / BK;
@@ -881,15 +880,19 @@ __device__ __forceinline__ void gemm_tiles(
     const long long first = (long long)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t rowB = (uint32_t)N * 2;            // bytes per weight row in memory
 
-    // fragment read offsets: A row (wm*WTM + 16 fm + l16) chunk lq; W rows 8 lq + (l16 >> 2)
-    const int a_rd = (wm * WTM + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
-    // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
-    const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
-    const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
-
     float* const pbuf = GATHER ? nullptr : part_buf;
     const WorkSplit wsp(total, G, pbuf ? KT : 0);
     for (long long w = first; w < wsp.nwork; w += G) {
+        // per-lane constants, derived here from an opaque copy of the thread index: kept
+        // live across the K loops they were spilled and reloaded at every item
+        int tid_o = threadIdx.x;
+        asm volatile("" : "+v"(tid_o));
+        const int lane = tid_o & 63, l16 = lane & 15, lq = lane >> 4;
+        // fragment read offsets: A row (wm*WTM + 16 fm + l16) chunk lq; W rows 8 lq + (l16 >> 2)
+        const int a_rd = (wm * WTM + l16) * (BK * 2) + ((lq ^ swa4(l16)) << 4);
+        // swizzle value of this lane's W rows (the same for rows k and k + 4 of its two reads)
+        const int g = BM == 320 ? fk320<NMAT>(8 * lq + (l16 >> 2)) : ((l16 >> 2) & 3) | ((lq & 1) << 2);
+        const int b_rd = (8 * lq + (l16 >> 2)) * BROW + (((l16 & 3) >> 1) << 4) + ((l16 & 1) << 3);
         // decode the work item (order: item_coords) and, for a split item, its part
         long long item;
         int part, slot;
