@@ -294,6 +294,54 @@ def test_forward_matches_oracle(lib, cfg):
         assert normwise(got[t], want) <= tol_for(cfg)
 
 
+POISON_CASES = [
+    # 256-row tiles with zipf-skewed counts: the ping-pong kernel's per-XCD queues, the
+    # stealing between them, thin tiles beside full ones
+    MoEConfig("poison_pp_skew", T=2048, H=264, E=16, k=2, F=392, ffn="swiglu", dtype="bf16", bias="zipf1.1"),
+    # a second projection with K = 4096: the split of the last round along K
+    MoEConfig("poison_pp_split", T=1024, H=136, E=4, k=2, F=4096, ffn="silu2", dtype="bf16", bias="none"),
+    # 320-row tiles with skewed counts (the four-wavefront kernel)
+    MoEConfig("poison_320", T=1200, H=520, E=16, k=3, F=392, ffn="silu2", dtype="bf16", bias="zipf1.1"),
+]
+
+
+@pytest.mark.parametrize("cfg", POISON_CASES, ids=[c.name for c in POISON_CASES])
+def test_forward_writes_every_row(lib, cfg):
+    """Every work item runs and nothing is read before this call writes it: after a clean
+    run (checked against the oracle), the workspace and the output are filled with 0xFF
+    bytes (NaN in bf16 and fp32) and the layer runs again, twice.  Every grouped row of h
+    and y and every output value must then be finite and the output equal, bit for bit,
+    to the clean run's (a skipped item would leave NaN rows; a counter or buffer read
+    before it is written would pick up the poison)."""
+    say(f"poisoned workspace {cfg}")
+    d = generate(cfg)
+    inp = {k: (None if v is None else v.cuda()) for k, v in d.items()}
+    ws = lib.Workspace()
+    args = (inp["x"], inp["w_gate"], inp["w_in"], inp["w_up"], inp["w_out"], cfg.k)
+    clean = lib.forward(*args, bias=inp["bias"], workspace=ws)
+    torch.cuda.synchronize()
+    mid = lib.forward_intermediates(ws, inp["x"], inp["w_gate"], inp["w_in"], inp["w_up"], cfg.k)
+    ref = _oracle_forward(cfg, d)
+    flips = check_selection(mid["topk_idx"].cpu().numpy(), ref["logits"], cfg.k)
+    got = to_numpy(clean)
+    keep = np.setdiff1d(np.arange(cfg.T), list(flips))
+    err = normwise(got[keep], ref["out"][keep])
+    say(f"  clean run: normwise error {err:.3e}, near-tie tokens {len(flips)}")
+    assert err <= tol_for(cfg)
+    clean = clean.clone()
+    out = torch.empty_like(clean)
+    for rep in range(2):
+        ws.buf.fill_(255)
+        out.view(torch.uint8).fill_(255)
+        lib.forward(*args, bias=inp["bias"], workspace=ws, out=out)
+        torch.cuda.synchronize()
+        mid = lib.forward_intermediates(ws, inp["x"], inp["w_gate"], inp["w_in"], inp["w_up"], cfg.k)
+        assert bool(torch.isfinite(mid["h"]).all()), f"run {rep}: rows of h left unwritten"
+        assert bool(torch.isfinite(mid["y"]).all()), f"run {rep}: rows of y left unwritten"
+        assert bool(torch.isfinite(out).all()), f"run {rep}: output values left unwritten"
+        assert torch.equal(out, clean), f"run {rep}: output differs from the clean run"
+
+
 @pytest.mark.parametrize("dtype,ffn", [("bf16", "silu2"), ("bf16", "swiglu"), ("f32", "swiglu")])
 def test_forward_all_tokens_to_two_experts(lib, dtype, ffn):
     """Degenerate routing: a logit bias of 40 on experts 3 and 6 sends every token to both, so
