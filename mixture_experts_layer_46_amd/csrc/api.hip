@@ -65,7 +65,7 @@ Layout layout_of(const moe_shape& s) {
     Layout L{};
     size_t o = 0;
     L.logits = o;       o += up((size_t)gate_splits(s.T, s.H, s.E, s.dtype) * s.T * s.E * 4);
-    L.planes = o;       o += gate_uses_planes(s.T, s.dtype) ? up((size_t)3 * s.E * s.H * 2) : 0;
+    L.planes = o;       o += gate_uses_planes(s.T, s.dtype) ? up((size_t)3 * s.E * gate_plane_k(s.H) * 2) : 0;
     L.topk_idx = o;     o += up(P * 4);
     L.topk_w = o;       o += up(P * 4);
     L.counts = o;       o += up((size_t)s.E * 4);

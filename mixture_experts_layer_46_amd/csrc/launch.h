@@ -45,10 +45,11 @@ void gemm_cfg_heights(GemmCfg c, int* bma, int* bmb);
 
 // K splits of the gate projection (partial sums [splits][T][E]) for a layer shape
 int gate_splits(long long T, int H, int E, int dtype);   // split-K ranges of the gate projection
-// whether the bf16 gate splits W_g into bf16 planes once per call (planes: 3 * E * H bf16
-// of workspace); `planes` NULL keeps the split inside each workgroup (moe_route, which has
-// no workspace)
+// whether the bf16 gate splits W_g into bf16 planes once per call (planes: 3 * E *
+// gate_plane_k(H) bf16 of workspace, K-step-major); `planes` NULL keeps the split inside
+// each workgroup (moe_route, which has no workspace)
 bool gate_uses_planes(long long T, int dtype);
+__host__ __device__ inline int gate_plane_k(int H) { return (H + 31) / 32 * 32; }   // H in whole K steps
 hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* out,
                               long long T, int H, int E, int splits, bf16_t* planes, hipStream_t st);
 // top-k over the sum of `nparts` partial logits; the sum goes to logits_out if not NULL

@@ -13,6 +13,8 @@
 // Top-k is one wavefront per token: each lane holds up to four experts, k rounds of a wave-wide arg-max pick
 // the winners ([FourStage §2.2]); gates are the softmax over the chosen logits,
 // which equals the full softmax renormalised over the k chosen ([Principles §2.2]).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -281,18 +283,40 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_x3(const bf16_t* __restr
     }
 }
 
-// W_g [H, E] fp32 -> three bf16 planes [3][E][H] (expert-major, k contiguous) with
-// w = p0 + p1 + p2 exactly (split3_bf16), once per call, so that the gate projection's
-// workgroups copy 16-byte runs of k instead of splitting and transposing weights each.
+// W_g [H, E] fp32 -> three bf16 planes with w = p0 + p1 + p2 exactly (split3_bf16), once
+// per call, so that the gate projection's workgroups copy runs of k instead of splitting
+// and transposing weights each.  Layout K-step-major, [H/32][3][E][32]: the 32 k of one
+// step of plane p and expert e are 64 contiguous bytes, and one step of one plane for 16
+// consecutive experts is 1 KB contiguous, so each direct-to-LDS load of the gate covers
+// whole cache lines.  Entries for k >= H (the last step's padding) are never written or read.
 // Tile: 64 k x 64 experts through LDS (loads coalesced along E, stores along k).
 __global__ __launch_bounds__(256) void k_gate_split_planes(const float* __restrict__ wg, bf16_t* __restrict__ planes,
                                                            int H, int E) {
     __shared__ float tile[64][65];
     const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64, tid = threadIdx.x;
-    for (int i = tid; i < 64 * 64; i += 256) {
-        const int r = i >> 6, c = i & 63;
-        const int k = k0 + r, e = e0 + c;
-        tile[r][c] = (k < H && e < E) ? wg[(size_t)k * E + e] : 0.f;
+    if ((E & 3) == 0 && ((uintptr_t)wg & 15) == 0) {   // whole 16-byte runs: 4 loads per thread
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, r = i >> 4, c = 4 * (i & 15);
+            const int k = k0 + r, e = e0 + c;
+            v[u] = (k < H && e < E) ? *reinterpret_cast<const float4*>(wg + (size_t)k * E + e)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, r = i >> 4, c = 4 * (i & 15);
+            tile[r][c] = v[u].x;
+            tile[r][c + 1] = v[u].y;
+            tile[r][c + 2] = v[u].z;
+            tile[r][c + 3] = v[u].w;
+        }
+    } else {
+        for (int i = tid; i < 64 * 64; i += 256) {
+            const int r = i >> 6, c = i & 63;
+            const int k = k0 + r, e = e0 + c;
+            tile[r][c] = (k < H && e < E) ? wg[(size_t)k * E + e] : 0.f;
+        }
     }
     __syncthreads();
     for (int i = tid; i < 64 * 8; i += 256) {
@@ -308,9 +332,11 @@ __global__ __launch_bounds__(256) void k_gate_split_planes(const float* __restri
                                     pack_bf16x2(m[6], m[7]));
         const uint4 vl = make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
                                     pack_bf16x2(l[6], l[7]));
-        *reinterpret_cast<uint4*>(planes + ((size_t)0 * E + e) * H + k) = vh;
-        *reinterpret_cast<uint4*>(planes + ((size_t)1 * E + e) * H + k) = vm;
-        *reinterpret_cast<uint4*>(planes + ((size_t)2 * E + e) * H + k) = vl;
+        // K step ks = k / 32 of plane p, expert e at ((ks * 3 + p) * E + e) * 32 + k % 32
+        const size_t base = ((size_t)(k >> 5) * 3 * E + e) * 32 + (k & 31);
+        *reinterpret_cast<uint4*>(planes + base) = vh;
+        *reinterpret_cast<uint4*>(planes + base + (size_t)E * 32) = vm;
+        *reinterpret_cast<uint4*>(planes + base + (size_t)2 * E * 32) = vl;
     }
 }
 
@@ -319,11 +345,13 @@ __global__ __launch_bounds__(256) void k_gate_split_planes(const float* __restri
 // of MFMAs against a load latency about twice as long).  Tile: 256 tokens x TE experts,
 // eight wavefronts in a 4 x 2 grid (64 tokens x TE/2 experts each, two per SIMD), K steps
 // of 32.  A stage holds x (256 rows of 64 bytes) and the three planes (3 TE rows of 64
-// bytes), rows swizzled with swa4 for the fragment reads; GS_NS stages, the DMA GS_LEAD
-// steps ahead, one barrier per step.  Every step issues the same DMA (steps past the K
-// range load zeros into a stage nobody reads), so each wavefront waits with a constant
-// count.  MFMA order per step and 16-expert block: the plane of the smallest parts first.
-constexpr int GS_NS = 4, GS_LEAD = GS_NS - 1;
+// bytes), rows swizzled with swa4 for the fragment reads.  The fragments of a step are
+// read into registers (two sets, alternating) a step ahead, so a stage is free once they
+// are: GS_NS stages hold the DMA of the next GS_NS steps, with one barrier per step in
+// the middle of its MFMAs.  Every step issues the same DMA (steps past the K range load
+// zeros into a stage nobody reads), so each wavefront waits with a constant count.  MFMA
+// order per step and 16-expert block: the plane of the smallest parts first.
+constexpr int GS_NS = 4;
 
 // keeps an accumulator in AGPRs (the MFMA then accumulates in place)
 __device__ __forceinline__ void gs_pin_acc(f32x4_t& a) { asm volatile("" : "+a"(a)); }
@@ -331,6 +359,9 @@ __device__ __forceinline__ void gs_pin_acc(f32x4_t& a) { asm volatile("" : "+a"(
 __device__ __forceinline__ void gs_dma(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
+// no instruction moves across this point (the MFMAs only touch registers, so the barrier's
+// memory clobber alone would let the scheduler hoist them above it)
+__device__ __forceinline__ void gs_sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // this wavefront's fragment reads are done, then every wavefront's (a bare s_barrier: the
 // fence of __syncthreads would also wait for the DMA in flight)
 __device__ __forceinline__ void gs_step_barrier() {
@@ -370,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
     const int kbeg = blockIdx.z * kchunk, kend = min(H, kbeg + kchunk);
     const int KT = kbeg < kend ? (kend - kbeg + BK - 1) / BK : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(planes, (uint32_t)((size_t)3 * E * H * 2));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(planes, (uint32_t)((size_t)3 * E * gate_plane_k(H) * 2));
     // this wavefront's DMA instructions j = wave + 8 i (j < NI): x rows 16 j .. 16 j + 15
     // for j < 16, else plane rows 16 (j - 16) ..; each lane moves one 16-byte chunk
     uint32_t off[DMAX], kq[DMAX];
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
                 if (t < T) off[i] = (uint32_t)(((size_t)t * H + kbeg + 8 * q) * 2);
             } else {
                 const int pl = r / TE, e = e0 + r % TE;
-                if (e < E) off[i] = (uint32_t)((((size_t)pl * E + e) * H + kbeg + 8 * q) * 2);
+                if (e < E) off[i] = (uint32_t)(((((size_t)(kbeg >> 5) * 3 + pl) * E + e) * 32 + 8 * q) * 2);
             }
         }
     }
@@ -401,14 +432,19 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
             const int j = wave + 8 * i;
             if (j < NI) {
                 const uint32_t dk = (uint32_t)step * BK;
-                const uint32_t o = (off[i] != kOOB && step < KT && kq[i] + dk < (uint32_t)kend) ? off[i] + dk * 2 : kOOB;
+                // a K step advances x rows by 64 bytes and the planes by one step block
+                const uint32_t adv = isx[i] ? (uint32_t)BK * 2 : (uint32_t)(3 * E * BK * 2);
+                const uint32_t o = (off[i] != kOOB && step < KT && kq[i] + dk < (uint32_t)kend) ? off[i] + (uint32_t)step * adv : kOOB;
                 gs_dma(isx[i] ? rx : rp, st + j * 1024, o);
             }
         }
     };
-    auto wait_step = [&]() {                    // this wavefront's DMA of the current step has landed
-        if (NI % 8 == 0 || wave < NI % 8) wait_vmcnt<S::DPW_HI * (GS_LEAD - 1)>();
-        else wait_vmcnt<S::DPW_LO * (GS_LEAD - 1)>();
+    // this wavefront's DMA of the step `ahead` steps back has landed (`ahead` later steps'
+    // DMA may still be in flight)
+    auto wait_dma = [&](auto ahead_c) {
+        constexpr int AH = decltype(ahead_c)::value;
+        if (NI % 8 == 0 || wave < NI % 8) wait_vmcnt<S::DPW_HI * AH>();
+        else wait_vmcnt<S::DPW_LO * AH>();
     };
     f32x4_t acc[FM][NB];
 #pragma unroll
@@ -431,36 +467,62 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
         const int r = wn * (TE / 2) + 16 * nb + fr;
         b_rd[nb] = S::X_BYTES + r * 64 + ((fq ^ swa4(r)) << 4);
     }
+    using LdsFrag = const __attribute__((address_space(3))) bf16x8_t;
+    auto read_frags = [&](int step, bf16x8_t (&a)[FM], bf16x8_t (&b)[NB][3]) {
+        const lds_char* cur = lds + (step % GS_NS) * S::BYTES;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) a[fm] = *(LdsFrag*)(cur + a_rd[fm]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) b[nb][p] = *(LdsFrag*)(cur + b_rd[nb] + p * TE * 64);
+    };
+    // the MFMAs of row blocks 2h, 2h + 1 (per 16-expert block: the plane of the smallest
+    // parts first)
+    auto mfma_half = [&](int h, const bf16x8_t (&a)[FM], const bf16x8_t (&b)[NB][3]) {
+#pragma unroll
+        for (int fm = 2 * h; fm < 2 * h + 2; ++fm)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
+                acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
+                acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
+            }
+    };
+    // Step s: half of its MFMAs from fragments already in registers, then the barrier
+    // (every wavefront's DMA of step s + 1 has landed and every read of stage s is done),
+    // the DMA of step s + GS_NS into the stage s just freed, the fragment reads of step
+    // s + 1 into the other register set, and the other half of the MFMAs, which cover
+    // the barrier and the read latency.
+    auto step = [&](int s, const bf16x8_t (&a)[FM], const bf16x8_t (&b)[NB][3], bf16x8_t (&an)[FM],
+                    bf16x8_t (&bn)[NB][3]) {
+        mfma_half(0, a, b);
+        gs_sched_fence();
+        wait_dma(std::integral_constant<int, GS_NS - 2>{});
+        gs_step_barrier();
+        dma(s + GS_NS);
+        read_frags(s + 1, an, bn);
+        gs_sched_fence();
+        mfma_half(1, a, b);
+        gs_sched_fence();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) gs_pin_acc(acc[fm][nb]);
+    };
     if (KT > 0) {
 #pragma unroll
-        for (int st = 0; st < GS_LEAD; ++st) dma(st);
-        for (int s = 0; s < KT; ++s) {
-            wait_step();
-            gs_step_barrier();                                  // reads of step s - 1 done; step s landed
-            dma(s + GS_LEAD);                                   // into the stage step s - 1 used
-            const lds_char* cur = lds + (s % GS_NS) * S::BYTES;
-            bf16x8_t a[FM], b[NB][3];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) a[fm] = *(const __attribute__((address_space(3))) bf16x8_t*)(cur + a_rd[fm]);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    b[nb][p] = *(const __attribute__((address_space(3))) bf16x8_t*)(cur + b_rd[nb] + p * TE * 64);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    // the small parts first
-                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][2], acc[fm][nb], 0, 0, 0);
-                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][1], acc[fm][nb], 0, 0, 0);
-                    acc[fm][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[nb][0], acc[fm][nb], 0, 0, 0);
-                }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gs_pin_acc(acc[fm][nb]);
+        for (int st = 0; st < GS_NS; ++st) dma(st);
+        wait_dma(std::integral_constant<int, GS_NS - 1>{});
+        gs_step_barrier();
+        bf16x8_t a0[FM], b0[NB][3], a1[FM], b1[NB][3];
+        read_frags(0, a0, b0);
+        int s = 0;
+        for (; s + 1 < KT; s += 2) {
+            step(s, a0, b0, a1, b1);
+            step(s + 1, a1, b1, a0, b0);
         }
+        if (s < KT) step(s, a0, b0, a1, b1);
         wait_vmcnt<0>();                        // the zero loads past the K range land before exit
     }
     float* o = out + (size_t)blockIdx.z * T * E;
@@ -479,41 +541,47 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
 }
 
 // ------------------------------------------------------------------------- top-k
-struct Cand {
-    float s;    // ranking score (l + b)
-    float g;    // value the gate is computed from
-    int i;      // expert index (>= E: empty)
-};
-
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-    // larger score first; equal scores (IEEE ==, so -0 == +0) to the lower index
-    return (a.s > b.s) || (a.s == b.s && a.i < b.i);
+// Ranking key of a score: keys compare as the scores do under IEEE ordering, with
+// -0 == +0 (both map to the key of +0); a NaN score gets key 0, below every number.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (s != s) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ Cand wave_best(Cand c) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        Cand o;
-        o.s = __shfl_xor(c.s, off);
-        o.g = __shfl_xor(c.g, off);
-        o.i = __shfl_xor(c.i, off);
-        if (o.i < 0x7fffffff && (c.i == 0x7fffffff || better(o, c))) c = o;
-    }
-    return c;
+// Inverse of score_key on numbers (NaN keys decode to a NaN).
+__device__ __forceinline__ float key_score(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// Reductions over each row of 16 lanes, the result in every lane of the row: DPP steps
+// that swap neighbours, swap pairs, mirror the half rows and mirror the rows.  Every
+// lane combines the same values in the same pairs, so a sum is the same bits in all 16.
+template <typename F>
+__device__ __forceinline__ uint32_t row_reduce_u32(uint32_t v, F op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    return row_reduce_u32(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+__device__ __forceinline__ float row_max_f32(float v) {
+    return __uint_as_float(row_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float row_sum_f32(float v) {
+    return __uint_as_float(row_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
 }
 
-// One wavefront per token, four tokens per workgroup.
+// Sixteen lanes per token, four tokens per wavefront, sixteen per workgroup; lane j of a
+// token's row holds experts j, j + 16, j + 32, ... (up to 256).
 // `logits` holds `nparts` partial sums [nparts][T][E] (split K); they are added in
 // order and, when `logits_out` is given, the sum is written there.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nparts,
@@ -522,61 +590,80 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
                                               int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w,
                                               long long T, int E, int k, unsigned flags) {
-    const int lane = threadIdx.x & 63;
-    const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    const int sub = threadIdx.x & 15;
+    const long long t_row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool row_live = t_row < T;
+    const long long t = row_live ? t_row : T - 1;   // a row past T repeats the last token, unstored
     const bool select_only = flags & MOE_FLAG_BIAS_SELECT_ONLY;
     const bool no_renorm = flags & MOE_FLAG_NO_RENORM;
-    float s[4], g[4], l[4];
-    bool live[4];
+    constexpr int NQ = 16;
+    float l[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        live[q] = lane + 64 * q < E;
-        l[q] = live[q] ? logits[t * E + lane + 64 * q] : 0.f;
+    for (int q = 0; q < NQ; ++q) {
+        const int e = sub + 16 * q;
+        l[q] = e < E ? logits[t * E + e] : 0.f;
     }
-    // the later partial sums, added in part order; loaded four parts at a time so that
-    // the loads are in flight together
-    for (int p = 1; p < nparts; p += 4) {
-        float v[4][4];
+    // the later partial sums, added in part order
+    for (int p = 1; p < nparts; ++p) {
+        const float* lp = logits + (long long)p * T * E + t * E;
+        float v[NQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ; ++q) v[q] = sub + 16 * q < E ? lp[sub + 16 * q] : 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[q][i] = (live[q] && p + i < nparts) ? logits[(long long)(p + i) * T * E + t * E + lane + 64 * q] : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (p + i < nparts) l[q] += v[q][i];
+        for (int q = 0; q < NQ; ++q) l[q] += v[q];
     }
+    // ranking keys of the scores l + b (one fp32 add), plus one; 0 marks no candidate
+    // (an expert past E, or one already chosen)
+    uint32_t key1[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        if (live[q] && logits_out) logits_out[t * E + e] = l[q];
-        const float b = (live[q] && bias) ? bias[e] : 0.f;
-        s[q] = l[q] + b;                    // one fp32 add: the ranking score
-        g[q] = select_only ? l[q] : s[q];   // what the gate is computed from
+    for (int q = 0; q < NQ; ++q) {
+        const int e = sub + 16 * q;
+        if (e < E && logits_out && row_live) logits_out[t * E + e] = l[q];
+        const float b = (e < E && bias) ? bias[e] : 0.f;
+        key1[q] = e < E ? score_key(l[q] + b) + 1u : 0u;   // keys stay below 0xFF800001
     }
+    // Selection: each round takes the largest key of the row, and of equal keys the
+    // lowest expert index (within a lane the first of equal keys is the lower index),
+    // and retires it.
     int sel_i[8];
-    float sel_g[8];
+    uint32_t sel_k[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         sel_i[j] = 0;
-        sel_g[j] = 0.f;
+        sel_k[j] = 0;
         if (j < k) {
-            Cand c{0.f, 0.f, 0x7fffffff};
+            uint32_t bk = 0;
+            int bq = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (!live[q]) continue;
-                const Cand o{s[q], g[q], lane + 64 * q};
-                if (c.i == 0x7fffffff || better(o, c)) c = o;
+            for (int q = 0; q < NQ; ++q) {
+                const bool take = key1[q] > bk;
+                bk = take ? key1[q] : bk;
+                bq = take ? q : bq;
             }
-            c = wave_best(c);
-            sel_i[j] = c.i;
-            sel_g[j] = c.g;
+            const uint32_t M = row_max_u32(bk);            // > 0: every row has k <= E experts
+            const uint32_t mine = (bk != 0u && bk == M) ? (uint32_t)(sub + 16 * bq) : 0xFFFFFFFFu;
+            const uint32_t ew = ~row_max_u32(~mine);        // the lowest expert index at key M
+            sel_i[j] = (int)ew;
+            sel_k[j] = M - 1u;
+            const int rq = mine == ew ? bq : -1;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (c.i == lane + 64 * q) live[q] = false;
+            for (int q = 0; q < NQ; ++q) key1[q] = q == rq ? 0u : key1[q];
+        }
+    }
+    // the values the gates come from: the ranking scores (decoded from the keys), or with
+    // the selection-only bias the raw logits of the chosen experts
+    float sel_g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sel_g[j] = key_score(sel_k[j]);
+        if (select_only && j < k) {
+            const int e = sel_i[j];
+            float own = 0.f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (sub + 16 * q == e) own = l[q];
+            // exactly one lane of the row holds expert e: the others contribute +0 bits
+            sel_g[j] = __uint_as_float(row_max_u32((e & 15) == sub ? __float_as_uint(own) : 0u));
         }
     }
     // gates: exp(g_j - m) / sum, m the largest g among the chosen (slot 0 unless the
@@ -589,28 +676,32 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     if (no_renorm) {
         // full softmax over every expert of the token
         float gm = -INFINITY;
+        float gv[NQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane + 64 * q < E) gm = fmaxf(gm, g[q]);
-        m = wave_max(gm);
+        for (int q = 0; q < NQ; ++q) {
+            const int e = sub + 16 * q;
+            gv[q] = (select_only || !bias || e >= E) ? l[q] : l[q] + bias[e];
+            if (e < E) gm = fmaxf(gm, gv[q]);
+        }
+        m = row_max_f32(gm);
         float part = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane + 64 * q < E) part += expf(g[q] - m);
-        den = wave_sum(part);
+        for (int q = 0; q < NQ; ++q)
+            if (sub + 16 * q < E) part += expf(gv[q] - m);
+        den = row_sum_f32(part);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             if (j < k) den += expf(sel_g[j] - m);
     }
-    if (lane < k) {
+    if (row_live && sub < k) {
         float gj = 0.f;
         int ij = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (j == lane) { gj = sel_g[j]; ij = sel_i[j]; }
-        topk_idx[t * k + lane] = ij;
-        topk_w[t * k + lane] = expf(gj - m) / den;
+            if (j == sub) { gj = sel_g[j]; ij = sel_i[j]; }
+        topk_idx[t * k + sub] = ij;
+        topk_w[t * k + sub] = expf(gj - m) / den;
     }
 }
 
@@ -623,7 +714,7 @@ int gate_tile_experts(long long T, int E, int dtype) {
 }
 
 // K ranges of the gate projection: enough workgroups for the CUs.  The bf16 tiles hold one
-// workgroup per CU (92 KB of LDS), so they aim at 256 workgroups; the fp32 tiles at 512.
+// workgroup per CU (160 KB of LDS), so they aim at 256 workgroups; the fp32 tiles at 512.
 int gate_splits(long long T, int H, int E, int dtype) {
     if (T <= 0) return 1;
     const long long tm = gate_tile_rows(T, dtype), te = gate_tile_experts(T, E, dtype);
@@ -676,7 +767,7 @@ hipError_t launch_gate_logits(const void* x, int dtype, const float* wg, float* 
 
 hipError_t launch_topk(const float* logits, int nparts, float* logits_out, const float* bias, int32_t* idx,
                        float* w, long long T, int E, int k, unsigned flags, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 15) / 16)), dim3(256), 0, st,
                        logits, nparts, logits_out, bias, idx, w, T, E, k, flags);
     return hipGetLastError();
 }

@@ -56,6 +56,27 @@ def test_route_from_logits_bit_exact(lib, T, E, k, use_bias, flags):
     np.testing.assert_allclose(w.cpu().numpy(), rg, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("E,k", [(256, 8), (100, 3), (64, 2)])
+def test_route_nonfinite_scores(lib, E, k):
+    """Scores of +inf, -inf and NaN: the selection is still the oracle's order (score
+    descending, NaN below every number, equal scores to the lower index)."""
+    say(f"route_nonfinite E={E} k={k}")
+    T = 96
+    g = torch.Generator().manual_seed(77 + E + k)
+    L = (torch.round(torch.randn(T, E, generator=g) * 2) / 4).float()
+    L[0::4, 5::9] = float("nan")
+    L[1::4, 3::7] = float("inf")
+    L[2::4, :: 2] = float("-inf")
+    L[3::4, :] = float("nan")
+    L[3::4, E - 1] = 1.0
+    L[3::8, 0] = float("-inf")
+    idx, _ = lib.route_from_logits(L.cuda(), k)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        _, ridx, _ = O.route_from_f32_logits(L.numpy(), None, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 # T > 256 with bf16 x takes the split-weight bf16 MFMA gate (128-token tiles); ragged
 # K (H = 200), several expert tiles (E = 256) and a ragged expert count (E = 37)
 ROUTE_X_CASES = [(333, 200, 64, 2), (1000, 4096, 256, 8), (700, 64, 37, 3), (200, 512, 64, 2),
