@@ -100,12 +100,27 @@ __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__
     const long long s = (long long)blockIdx.x * 4 + w;
     if (s >= NS) return;
     const uint64_t lt = lanemask_lt();
-    for (int r = 0; r < kSeg / 64; ++r) {
+    // the segment's expert ids, then their rank bases and offsets, all loaded before the
+    // ranking, so the segment costs two memory latencies instead of two per round
+    constexpr int R = kSeg / 64;
+    int ev[R], base[R], off[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const long long p = s * kSeg + r * 64 + lane;
+        ev[r] = p < P ? idx[p] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool valid = (unsigned)ev[r] < (unsigned)E;
+        base[r] = valid ? segbase[s * E + ev[r]] : 0;
+        off[r] = valid ? offsets[ev[r]] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
         const long long p = s * kSeg + r * 64 + lane;
         const bool inside = p < P;
-        const int raw = inside ? idx[p] : 0;
-        const bool valid = inside && (unsigned)raw < (unsigned)E;
-        const int e = valid ? raw : 0;
+        const bool valid = inside && (unsigned)ev[r] < (unsigned)E;
+        const int e = valid ? ev[r] : 0;
         // lanes of this round holding the same expert id
         uint64_t same = ballot64(valid);
         for (int b = 0; b < nbits; ++b) {
@@ -116,8 +131,8 @@ __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__
         const int before = __popcll(same & lt);
         int row = -1;
         if (valid) {
-            const int rank = segbase[s * E + e] + run[w][e] + before;
-            if (capacity <= 0 || rank < capacity) row = offsets[e] + rank;
+            const int rank = base[r] + run[w][e] + before;
+            if (capacity <= 0 || rank < capacity) row = off[r] + rank;
         }
         __builtin_amdgcn_wave_barrier();
         if (valid && before == 0) run[w][e] += __popcll(same);   // one leader per expert

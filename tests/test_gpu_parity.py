@@ -77,6 +77,27 @@ def test_route_nonfinite_scores(lib, E, k):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
+@pytest.mark.parametrize("E,k", [(256, 8), (200, 8), (48, 3)])
+def test_route_winners_in_one_lane(lib, E, k):
+    """The k largest scores of a token all on experts that share e mod 16 (one lane of
+    the selection holds them), some of them equal: the order is still score
+    descending, then index ascending."""
+    say(f"route_one_lane E={E} k={k}")
+    T = 80
+    g = torch.Generator().manual_seed(4242 + E + k)
+    L = (torch.round(torch.randn(T, E, generator=g) * 2) / 8).float()
+    for r in range(T):
+        lane = r % 16
+        owned = list(range(lane, E, 16))
+        for i, e in enumerate(owned[:k + 1]):
+            L[r, e] = 10.0 - (i // 2)          # pairs of equal scores
+    idx, w = lib.route_from_logits(L.cuda(), k)
+    torch.cuda.synchronize()
+    _, ridx, rg = O.route_from_f32_logits(L.numpy(), None, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rg, rtol=1e-6, atol=1e-7)
+
+
 # T > 256 with bf16 x takes the split-weight bf16 MFMA gate (128-token tiles); ragged
 # K (H = 200), several expert tiles (E = 256) and a ragged expert count (E = 37)
 ROUTE_X_CASES = [(333, 200, 64, 2), (1000, 4096, 256, 8), (700, 64, 37, 3), (200, 512, 64, 2),
