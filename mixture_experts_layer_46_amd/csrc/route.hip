@@ -10,9 +10,9 @@
 // MFMA (v_mfma_f32_16x16x4_f32): exact widening of bf16 x, fp32 products and
 // accumulation.  For bf16 x it runs on the bf16 MFMA with the weights split exactly
 // into three bf16 parts (k_gate_logits_x3): the same fp32 products and accumulation.
-// Top-k is one wavefront per token: each lane holds up to four experts, k rounds of a wave-wide arg-max pick
-// the winners ([FourStage §2.2]); gates are the softmax over the chosen logits,
-// which equals the full softmax renormalised over the k chosen ([Principles §2.2]).
+// Top-k takes 16 lanes per token, each holding up to 16 experts; k rounds of a row-wide
+// arg-max pick the winners ([FourStage §2.2]); gates are the softmax over the chosen
+// logits, which equals the full softmax renormalised over the k chosen ([Principles §2.2]).
 #include <type_traits>
 
 #include "common.h"
