@@ -42,7 +42,9 @@
  * T * k < 2^31; T*k*max(H,F) < 4e18 elements; x (T*H elements) and one expert matrix
  * with 128 extra rows ((H+128)*F and (F+128)*H elements) below 2 GiB each, since the
  * grouped GEMM reads them through buffer resources with 32-bit byte offsets and an
- * out-of-range marker at 2^31 (MOE_ERR_UNSUPPORTED otherwise).
+ * out-of-range marker at 2^31; for bf16 x and T > 256 the gate's weight planes
+ * (3 * E * H rounded up to a multiple of 32, bf16) below 2 GiB too, for the same
+ * reason (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -116,6 +116,10 @@ moe_status check_shape(const moe_shape* s) {
                     s->H, s->F);
     if (s->T * (long long)s->H * es >= (1ll << 31))
         return fail(MOE_ERR_UNSUPPORTED, "x (T=%lld x H=%d) must stay below 2 GiB", (long long)s->T, s->H);
+    // the bf16 gate's weight planes are read the same way
+    if (gate_uses_planes(s->T, s->dtype) && 3ll * s->E * gate_plane_k(s->H) * 2 >= (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "the gate's weight planes (3 x E=%d x H=%d bf16) must stay below 2 GiB",
+                    s->E, s->H);
     return MOE_OK;
 }
 

@@ -70,6 +70,8 @@ def _ws(lib, s):
     (dict(H=65536, F=32768), 3), (dict(H=8, F=1 << 24), 3), (dict(T=300000, H=8192), 3),
     (dict(H=16384, F=65536), 3), (dict(T=131072, H=8192), 3),
     (dict(H=8, F=(1 << 30) // 136 // 8 * 8 + 8), 3),
+    # the bf16 gate's weight planes (3 x E x H rounded up to 32, bf16) of 2 GiB or more
+    (dict(T=300, H=1398088, E=256), 3),
 ])
 def test_bad_shapes_are_rejected(lib, kw, code):
     s = _shape(**kw)
@@ -160,6 +162,12 @@ def test_largest_accepted_shapes(lib):
     assert lib.moe_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == 0
     ok2 = _shape(T=(1 << 30) // 8192 - 1, H=8192)
     assert lib.moe_workspace_size(ctypes.byref(ok2), ctypes.byref(n)) == 0
+    # the gate's weight planes just below 2 GiB (3 * 256 * 1398080 * 2 bytes), and above it
+    # for fp32 x, whose gate reads W_g directly
+    ok3 = _shape(T=300, H=1398080, E=256)
+    assert lib.moe_workspace_size(ctypes.byref(ok3), ctypes.byref(n)) == 0
+    ok4 = _shape(T=300, H=1398088, E=256, dtype=_lib.MOE_F32)
+    assert lib.moe_workspace_size(ctypes.byref(ok4), ctypes.byref(n)) == 0
 
 
 def test_capacity_rows(lib):
