@@ -581,7 +581,7 @@ __device__ __forceinline__ float row_sum_f32(float v) {
 }
 
 // Sixteen lanes per token, four tokens per wavefront, sixteen per workgroup; lane j of a
-// token's row holds experts j, j + 16, j + 32, ... (up to 256).
+// token's row holds experts 4j .. 4j + 3, 64 + 4j .. 64 + 4j + 3, ... (up to 256).
 // `logits` holds `nparts` partial sums [nparts][T][E] (split K); they are added in
 // order and, when `logits_out` is given, the sum is written there.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nparts,
@@ -597,18 +597,33 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     const bool select_only = flags & MOE_FLAG_BIAS_SELECT_ONLY;
     const bool no_renorm = flags & MOE_FLAG_NO_RENORM;
     constexpr int NQ = 16;
-    float l[NQ];
+    // expert of slot q: four runs of four consecutive experts, 64 apart, so that one
+    // 16-byte load per lane reads 256 contiguous bytes of a token's row; within a lane
+    // the slots run in expert order
+    auto eid = [&](int q) { return 4 * sub + 64 * (q >> 2) + (q & 3); };
+    const bool vec = (E & 3) == 0 && ((uintptr_t)logits & 15) == 0;
+    auto load_part = [&](const float* row, float (&v)[NQ]) {
+        if (vec) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int e = sub + 16 * q;
-        l[q] = e < E ? logits[t * E + e] : 0.f;
-    }
+            for (int gq = 0; gq < NQ / 4; ++gq) {
+                const int e0 = eid(4 * gq);
+                const float4 f = e0 < E ? *reinterpret_cast<const float4*>(row + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[4 * gq] = f.x;
+                v[4 * gq + 1] = f.y;
+                v[4 * gq + 2] = f.z;
+                v[4 * gq + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) v[q] = eid(q) < E ? row[eid(q)] : 0.f;
+        }
+    };
+    float l[NQ];
+    load_part(logits + t * E, l);
     // the later partial sums, added in part order
     for (int p = 1; p < nparts; ++p) {
-        const float* lp = logits + (long long)p * T * E + t * E;
         float v[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) v[q] = sub + 16 * q < E ? lp[sub + 16 * q] : 0.f;
+        load_part(logits + (long long)p * T * E + t * E, v);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) l[q] += v[q];
     }
@@ -617,7 +632,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     uint32_t key1[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int e = sub + 16 * q;
+        const int e = eid(q);
         if (e < E && logits_out && row_live) logits_out[t * E + e] = l[q];
         const float b = (e < E && bias) ? bias[e] : 0.f;
         key1[q] = e < E ? score_key(l[q] + b) + 1u : 0u;   // keys stay below 0xFF800001
@@ -641,7 +656,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
                 bq = take ? q : bq;
             }
             const uint32_t M = row_max_u32(bk);            // > 0: every row has k <= E experts
-            const uint32_t mine = (bk != 0u && bk == M) ? (uint32_t)(sub + 16 * bq) : 0xFFFFFFFFu;
+            const uint32_t mine = (bk != 0u && bk == M) ? (uint32_t)eid(bq) : 0xFFFFFFFFu;
             const uint32_t ew = ~row_max_u32(~mine);        // the lowest expert index at key M
             sel_i[j] = (int)ew;
             sel_k[j] = M - 1u;
@@ -661,9 +676,9 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
             float own = 0.f;
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                if (sub + 16 * q == e) own = l[q];
+                if (eid(q) == e) own = l[q];
             // exactly one lane of the row holds expert e: the others contribute +0 bits
-            sel_g[j] = __uint_as_float(row_max_u32((e & 15) == sub ? __float_as_uint(own) : 0u));
+            sel_g[j] = __uint_as_float(row_max_u32(((e & 63) >> 2) == sub ? __float_as_uint(own) : 0u));
         }
     }
     // gates: exp(g_j - m) / sum, m the largest g among the chosen (slot 0 unless the
@@ -679,7 +694,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
         float gv[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int e = sub + 16 * q;
+            const int e = eid(q);
             gv[q] = (select_only || !bias || e >= E) ? l[q] : l[q] + bias[e];
             if (e < E) gm = fmaxf(gm, gv[q]);
         }
@@ -687,7 +702,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
         float part = 0.f;
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            if (sub + 16 * q < E) part += expf(gv[q] - m);
+            if (eid(q) < E) part += expf(gv[q] - m);
         den = row_sum_f32(part);
     } else {
 #pragma unroll
