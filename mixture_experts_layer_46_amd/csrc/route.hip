@@ -439,8 +439,8 @@ __global__ __launch_bounds__(512, 1) void k_gate_logits_p3(const bf16_t* __restr
             }
         }
     };
-    // this wavefront's DMA of the step `ahead` steps back has landed (`ahead` later steps'
-    // DMA may still be in flight)
+    // every DMA this wavefront issued has landed except the last `ahead` steps' (which may
+    // still be in flight)
     auto wait_dma = [&](auto ahead_c) {
         constexpr int AH = decltype(ahead_c)::value;
         if (NI % 8 == 0 || wave < NI % 8) wait_vmcnt<S::DPW_HI * AH>();
